@@ -1,0 +1,358 @@
+"""Pins of the oracle's transform, scales and quantizers.
+
+Each test checks the oracle against a closed form, an invariant the pages or
+the mathematics fix, a library routine, or brute force on a tiny input:
+* RHT: the recovered matrix equals 1/4 * Sylvester H16 * diag(sigma) with
+  H[i][j] = (-1)^popcount(i & j) (closed form), H H^T = 16 I in integers,
+  norms and inner products preserved within fp32 rounding ("Pretraining Large
+  Language Models with NVFP4", section 2B.2: the transform spreads outliers and
+  is applied to both Wgrad inputs, whose product it must therefore preserve).
+* tensor scale: amax = 2688 * 2^k gives S_enc = 2^-k exactly; 0 gives 1.
+* two-level scaling (section 2A): the element that holds the global amax
+  encodes to +-6 under the largest scale byte 0x7E; every block whose byte is
+  a normal E4M3 encodes its own amax element to +-6 ("outliers kept at
+  near-FP8 precision"); a round trip of representable values is exact.
+* symmetry, scaling by powers of two, monotonicity within a block.
+* columnwise copy equals the rowwise quantization of the transpose.
+* 2D (section 2B.3): quantize_2d(W)^T == quantize_2d(W^T), and the
+  transposed copy equals both; 2D equals 1D when all rows of a tile share the
+  same block amax.
+* SR on whole tensors: brute force against the codec on a tiny tensor, and
+  the rounding is unbiased.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_block_scaled_quant_amd import datagen
+
+
+def unpack(codes):
+    """[r][c/2] bytes -> [r][c] nibbles, even element in the low nibble."""
+    lo = codes & 0x0F
+    hi = codes >> 4
+    return np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
+
+
+def sylvester16():
+    i = np.arange(16)
+    pc = np.vectorize(lambda v: bin(v).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1, -1)
+
+
+# ------------------------------------------------------------------ RHT ---
+@pytest.mark.parametrize("seed", [0, 7, 2**40 + 3])
+def test_rht_is_scaled_sylvester_with_signs(orc, seed):
+    eye = np.eye(16, dtype=np.float32)
+    y = orc.rht(eye, seed)  # row j = transform of e_j = 1/4 * sigma_j * H[:, j]
+    mask = orc.rht_sign_mask(seed)
+    sigma = np.array([-1 if (mask >> j) & 1 else 1 for j in range(16)])
+    H = sylvester16()
+    assert np.array_equal(y.T.astype(np.float64), 0.25 * H * sigma[None, :])
+    Hr = np.rint(4 * y.T * sigma[None, :]).astype(np.int64)
+    assert np.array_equal(Hr @ Hr.T, 16 * np.eye(16, dtype=np.int64))
+
+
+def test_rht_exact_on_small_integers(orc):
+    rng = np.random.default_rng(0)
+    x = rng.integers(-64, 65, size=(64, 48)).astype(np.float32)
+    y = orc.rht(x, 11)
+    mask = orc.rht_sign_mask(11)
+    sigma = np.array([-1 if (mask >> j) & 1 else 1 for j in range(16)])
+    M = 0.25 * sylvester16() * sigma[None, :]
+    want = (x.reshape(64, 3, 16).astype(np.float64) @ M.T).reshape(64, 48)
+    assert np.array_equal(y.astype(np.float64), want)
+
+
+def test_rht_preserves_norm_and_products(orc):
+    rng = np.random.default_rng(1)
+    a = rng.standard_normal((32, 256)).astype(np.float32)
+    b = rng.standard_normal((32, 256)).astype(np.float32)
+    ya, yb = orc.rht(a, 3).astype(np.float64), orc.rht(b, 3).astype(np.float64)
+    a64, b64 = a.astype(np.float64), b.astype(np.float64)
+    assert np.allclose(np.linalg.norm(ya, axis=1), np.linalg.norm(a64, axis=1), rtol=1e-6)
+    assert np.allclose((ya * yb).sum(1), (a64 * b64).sum(1), atol=1e-4 * 16)
+
+
+def test_rht_spreads_an_outlier(orc):
+    x = np.zeros((1, 16), dtype=np.float32)
+    x[0, 5] = 100.0
+    y = orc.rht(x, 0)
+    assert np.allclose(np.abs(y), 25.0)
+
+
+def test_rht_bf16_input_equals_f32_input(orc):
+    t = datagen.sweep(32, 64, seed=4)
+    a = orc.rht(datagen.bf16_bits(t), 9)
+    b = orc.rht(t.float().numpy(), 9)
+    assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------- tensor scale ---
+def test_tensor_scale_closed_forms(orc):
+    for k in range(-20, 21):
+        assert orc.tensor_scale(2688.0 * 2.0 ** k) == 2.0 ** -k
+    assert orc.tensor_scale(0.0) == 1.0
+    assert orc.tensor_scale(1e-44) == np.finfo(np.float32).max
+    assert orc.tensor_scale(6.0) == np.float32(448.0)
+
+
+# ----------------------------------------------------------- quantizers ---
+def small_act(rows=64, cols=96, seed=0):
+    return datagen.act(tokens=rows, hidden=cols, seed=seed)
+
+
+def test_global_amax_element_encodes_to_six(orc):
+    t = small_act()
+    x = datagen.bf16_bits(t)
+    codes, scales, ts, _, _ = orc.quantize_1d(x)
+    xf = t.float().numpy()
+    r, c = np.unravel_index(np.argmax(np.abs(xf)), xf.shape)
+    assert ts[1] == np.abs(xf).max()
+    assert ts[0] == np.float32(2688.0) / np.float32(ts[1])
+    assert scales[r, c // 16] == 0x7E
+    assert unpack(codes)[r, c] & 7 == 7
+
+
+def test_block_amax_encodes_to_six_in_normal_blocks(orc):
+    t = small_act(128, 160, seed=3)
+    xf = t.float().numpy()
+    codes, scales, _, _, _ = orc.quantize_1d(datagen.bf16_bits(t))
+    q = unpack(codes)
+    blocks = np.abs(xf).reshape(128, 10, 16)
+    arg = blocks.argmax(-1)
+    normal = (scales >> 3) & 0xF > 0
+    for r in range(128):
+        for b in range(10):
+            if normal[r, b] and blocks[r, b].max() > 0:
+                assert q[r, b * 16 + arg[r, b]] & 7 == 7
+
+
+def test_round_trip_of_representable_values(orc):
+    rng = np.random.default_rng(7)
+    rows, cols = 64, 128
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    q = rng.choice(grid, size=(rows, cols)) * rng.choice([-1, 1], size=(rows, cols))
+    q.reshape(rows, cols // 16, 16)[:, :, 0] = 6.0  # every block reaches 6
+    byte = rng.integers(0x08, 0x70, size=(rows, cols // 16))  # normal scales <= 2^7
+    sb = np.array([orc.e4m3_value(b) for b in range(256)])[byte]
+    x = (q.reshape(rows, cols // 16, 16) * sb[:, :, None]).reshape(rows, cols)
+    x = np.concatenate([x, np.zeros((16, cols))], 0)
+    x[rows, 0] = 2688.0  # amax -> S_enc = 1, block byte 0x7E
+    x = x.astype(np.float32)
+    codes, scales, ts, _, _ = orc.quantize_1d(x)
+    assert ts[0] == 1.0
+    assert np.array_equal(scales[:rows], byte)
+    deq = orc.dequantize(codes, scales, ts[0])
+    assert np.array_equal(deq[:rows], x[:rows].astype(np.float64))
+    # stochastic rounding reproduces them too when the scales are powers of two
+    pow2 = (byte & ~7)  # mantissa 0 -> exact reciprocal
+    sb2 = np.array([orc.e4m3_value(b) for b in range(256)])[pow2]
+    x2 = x.copy()
+    x2[:rows] = (q.reshape(rows, cols // 16, 16) * sb2[:, :, None]).reshape(rows, cols)
+    c2, s2, t2, _, _ = orc.quantize_1d(x2, rounding=1, seed=5)
+    assert np.array_equal(orc.dequantize(c2, s2, t2[0])[:rows], x2[:rows].astype(np.float64))
+
+
+def test_sign_symmetry_rne(orc):
+    t = small_act(48, 64, seed=2)
+    x = t.float().numpy()
+    a = orc.quantize_1d(x)
+    b = orc.quantize_1d(-x)
+    assert np.array_equal(a[1], b[1])
+    assert np.array_equal(unpack(a[0]) ^ 8, unpack(b[0]))
+
+
+def test_power_of_two_scaling_invariance(orc):
+    t = small_act(48, 64, seed=5)
+    x = t.float().numpy()
+    base = orc.quantize_1d(x)
+    for k in (-6, -1, 3, 9):
+        s = orc.quantize_1d((x * 2.0 ** k).astype(np.float32))
+        assert np.array_equal(base[0], s[0]) and np.array_equal(base[1], s[1])
+        assert s[2][0] == base[2][0] * 2.0 ** -k
+
+
+def test_monotone_within_block(orc):
+    rng = np.random.default_rng(9)
+    x = np.sort(rng.standard_normal((40, 32)).astype(np.float32), axis=1)
+    x[0, 0] = -50
+    codes, scales, ts, _, _ = orc.quantize_1d(x)
+    deq = orc.dequantize(codes, scales, ts[0])
+    for r in range(40):
+        for b in range(2):
+            seg = deq[r, b * 16:(b + 1) * 16]
+            assert np.all(np.diff(seg) >= 0)
+
+
+def test_zero_tensor_and_zero_blocks(orc):
+    x = np.zeros((16, 32), dtype=np.float32)
+    x[3, 20:] = -0.0
+    codes, scales, ts, ct, st = orc.quantize_1d(x, transposed=True)
+    assert ts[0] == 1.0 and ts[1] == 0.0
+    assert not scales.any()
+    assert np.array_equal(unpack(codes)[3, 20:], np.full(12, 8))
+    assert unpack(codes)[3, :20].max() == 0
+
+
+def test_columnwise_equals_rowwise_of_transpose(orc):
+    t = small_act(64, 48, seed=6)
+    x = datagen.bf16_bits(t)
+    _, _, ts, ct, st = orc.quantize_1d(x, transposed=True)
+    xt = np.ascontiguousarray(x.T)
+    c2, s2, ts2, _, _ = orc.quantize_1d(xt)
+    assert np.array_equal(ct, c2) and np.array_equal(st, s2) and np.array_equal(ts, ts2)
+
+
+def test_2d_transpose_consistency(orc):
+    w = datagen.weight(out_features=96, in_features=64, seed=1)
+    x = datagen.bf16_bits(w)
+    codes, scales, ts, ct, st = orc.quantize_2d(x)
+    xt = np.ascontiguousarray(x.T)
+    c2, s2, ts2, ct2, st2 = orc.quantize_2d(xt)
+    assert np.array_equal(ct, c2) and np.array_equal(st, s2)
+    assert np.array_equal(codes, ct2) and np.array_equal(scales, st2)
+    assert np.array_equal(unpack(ct), unpack(codes).T)
+    # the tile byte is replicated on the 16 rows of the tile
+    assert np.array_equal(scales, np.repeat(scales[::16], 16, axis=0))
+
+
+def test_2d_transpose_consistency_sr(orc):
+    w = datagen.weight(out_features=64, in_features=32, seed=2)
+    codes, scales, ts, ct, st = orc.quantize_2d(datagen.bf16_bits(w), rounding=1, seed=3)
+    assert np.array_equal(unpack(ct), unpack(codes).T)
+
+
+def test_2d_equals_1d_when_rows_share_block_amax(orc):
+    rng = np.random.default_rng(4)
+    rows, cols = 32, 48
+    x = rng.uniform(-1, 1, size=(rows, cols)).astype(np.float32)
+    x.reshape(rows, cols // 16, 16)[:, :, 3] = 1.5  # every 1x16 block has amax 1.5
+    a = orc.quantize_1d(x)
+    b = orc.quantize_2d(x, transposed=False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_sr_tensor_brute_force(orc):
+    rows, cols = 16, 32
+    t = small_act(rows, cols, seed=8)
+    xf = t.float().numpy()
+    seed = 77
+    codes, scales, ts, ct, st = orc.quantize_1d(datagen.bf16_bits(t), rounding=1, seed=seed,
+                                                transposed=True)
+    s_enc = ts[0]
+    q = unpack(codes)
+    for r in range(rows):
+        for b in range(cols // 16):
+            sb = np.float32(orc.e4m3_value(scales[r, b]))
+            inv = np.float32(s_enc) / sb if sb != 0 else np.float32(0)
+            for j in range(16):
+                c = b * 16 + j
+                y = np.float32(xf[r, c]) * inv
+                u = orc.sr_bits(seed, 0, r * cols + c)
+                assert q[r, c] == orc.e2m1_encode_sr(y, u)
+    qt = unpack(ct)
+    for c in range(cols):
+        sb = np.float32(orc.e4m3_value(st[c, 0]))
+        inv = np.float32(s_enc) / sb
+        for r in range(rows):
+            y = np.float32(xf[r, c]) * inv
+            assert qt[c, r] == orc.e2m1_encode_sr(y, orc.sr_bits(seed, 1, c * rows + r))
+
+
+def test_sr_unbiased_over_tensor(orc):
+    # a tensor whose blocks all decode with S_enc = 1 and scale 1: values swept
+    # over every grid interval; mean of the decoded values ~ the value
+    rows = 4096
+    vals = np.linspace(0.01, 5.99, 15).astype(np.float32)
+    x = np.tile(np.concatenate([[6.0], vals]).astype(np.float32), (rows, 1))
+    x = np.concatenate([x, np.zeros((1, 16), np.float32)])
+    x[rows, 0] = 2688.0
+    codes, scales, ts, _, _ = orc.quantize_1d(x, rounding=1, seed=123)
+    assert ts[0] == 1.0 and (scales[:rows] == 0x38).all()
+    deq = orc.dequantize(codes, scales, 1.0)[:rows, 1:]
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    for j, v in enumerate(vals):
+        lo = grid[grid <= v].max()
+        hi = grid[grid > v].min()
+        p = (v - lo) / (hi - lo)
+        sigma = (hi - lo) * np.sqrt(p * (1 - p) / rows)
+        assert abs(deq[:, j].mean() - v) < 5 * sigma + 1e-12
+
+
+def test_rht_fused_equals_composed(orc):
+    t = datagen.grad(tokens=32, out_features=64, seed=1)
+    x = datagen.bf16_bits(t)
+    fused = orc.quantize_1d(x, rounding=1, seed=3, rht=1, rht_seed=5)
+    y = orc.rht(x, 5)
+    comp = orc.quantize_1d(y, rounding=1, seed=3)
+    for a, b in zip(fused[:3], comp[:3]):
+        assert np.array_equal(a, b)
+
+
+def test_bad_arguments(orc):
+    x = np.zeros((16, 24), dtype=np.float32)
+    with pytest.raises(orc.OracleError):
+        orc.quantize_1d(x)  # 24 is not a multiple of 16
+    x = np.zeros((8, 16), dtype=np.float32)
+    with pytest.raises(orc.OracleError):
+        orc.quantize_2d(x)
+    with pytest.raises(orc.OracleError):
+        orc.quantize_1d(x, transposed=True)  # 8 rows
+    x = np.zeros((16, 16), dtype=np.float32)
+    x[1, 1] = np.nan
+    with pytest.raises(orc.OracleError):
+        orc.quantize_1d(x)
+    x[1, 1] = np.inf
+    with pytest.raises(orc.OracleError):
+        orc.quantize_1d(x)
+
+
+def test_ties_and_thresholds_through_the_quantizer(orc):
+    """Values that land exactly on E2M1 ties (RNE) and on exact SR fractions,
+    with S_enc = 1 and power-of-two block scales so that y = x / 2^k exactly.
+    A one-ulp error anywhere in S_enc, the block multiplier or y moves a tie."""
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    even = np.array([0, 2, 2, 4, 4, 6, 6])
+    rows, blocks = 8, 4
+    x = np.zeros((rows + 1, blocks * 16), dtype=np.float64)
+    for r in range(rows):
+        for b in range(blocks):
+            k = (r * blocks + b) % 9 - 4  # block scale 2^k, byte 0x38 + 8k
+            seg = np.concatenate([[6.0], ties, -ties, [0.0]]) * 2.0 ** k
+            x[r, b * 16:(b + 1) * 16] = seg
+    x[rows, 0] = 2688.0
+    x = x.astype(np.float32)
+    codes, scales, ts, _, _ = orc.quantize_1d(x)
+    assert ts[0] == 1.0
+    q = unpack(codes)
+    for r in range(rows):
+        for b in range(blocks):
+            k = (r * blocks + b) % 9 - 4
+            assert scales[r, b] == 0x38 + 8 * k
+            blk = q[r, b * 16:(b + 1) * 16]
+            assert blk[0] == 7
+            assert np.array_equal(blk[1:8], even)
+            assert np.array_equal(blk[8:15], even | 8)
+    # SR: y = lo + f * step with f = m / 65536 exactly; up iff u < m
+    rng = np.random.default_rng(11)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    n = 4096
+    lo_i = rng.integers(0, 7, n)
+    mnum = rng.integers(1, 65536, n)
+    y = grid[lo_i] + (grid[lo_i + 1] - grid[lo_i]) * mnum / 65536.0
+    xs = np.zeros((n // 15 + 2, 16))
+    flat = np.full(((n // 15 + 1) * 15,), 0.0)
+    flat[:n] = y
+    xs[:-1, 0] = 6.0
+    xs[:-1, 1:] = flat.reshape(-1, 15)
+    xs[-1, 0] = 2688.0
+    xs = xs.astype(np.float32)
+    assert np.array_equal(xs[:-1, 1:].reshape(-1)[:n].astype(np.float64), y)
+    c2, s2, t2, _, _ = orc.quantize_1d(xs, rounding=1, seed=99)
+    q2 = unpack(c2)[:-1, 1:].reshape(-1)[:n]
+    cols = 16
+    idx = np.array([(i // 15) * cols + 1 + (i % 15) for i in range(n)])
+    u = np.array([orc.sr_bits(99, 0, int(t)) for t in idx])
+    up = u < mnum
+    assert np.array_equal(q2 & 7, np.where(up, lo_i + 1, lo_i))
