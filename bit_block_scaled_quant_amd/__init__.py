@@ -1,0 +1,182 @@
+"""NVFP4 quantizer and block-scaled FP4 GEMM for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libnvfp4.so`` (C ABI in ``include/nvfp4.h``).
+The functions named like the C entry points (``nvfp4_quantize``,
+``nvfp4_quantize_2d``, ``nvfp4_rht``, ``nvfp4_gemm``) only marshal torch
+tensors into pointers and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no CPU fallback: if
+the library is missing, or a tensor is not on the GPU, the call raises.
+
+Convenience wrappers (``quantize``, ``quantize_2d``, ``rht``, ``gemm``)
+allocate the outputs with torch (device memory only) and call the same
+entry points.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+F32, BF16 = 0, 1
+RNE, SR = 0, 1
+STATUS = {0: "ok", -1: "invalid argument", -2: "invalid shape", -3: "misaligned pointer",
+          -4: "HIP error"}
+
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status, where, detail=""):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)}"
+        if detail:
+            msg += f" ({detail})"
+        super().__init__(msg)
+
+
+def lib():
+    """Load libnvfp4.so (built by ``build.py``); raise if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built: run bit_block_scaled_quant_amd/build.py "
+                              "(hipcc, gfx950); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, U64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int
+        L.nvfp4_quantize.restype = I
+        L.nvfp4_quantize.argtypes = [P, I, I64, I64, I, U64, I, U64, P, P, P, P, P, P]
+        L.nvfp4_quantize_2d.restype = I
+        L.nvfp4_quantize_2d.argtypes = [P, I, I64, I64, I, U64, P, P, P, P, P, P]
+        L.nvfp4_rht.restype = I
+        L.nvfp4_rht.argtypes = [P, I, I64, I64, U64, P, P]
+        L.nvfp4_gemm.restype = I
+        L.nvfp4_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, P]
+        L.nvfp4_status_string.restype = ctypes.c_char_p
+        L.nvfp4_status_string.argtypes = [I]
+        L.nvfp4_last_error.restype = ctypes.c_char_p
+        L.nvfp4_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(rc, where):
+    if rc != 0:
+        detail = lib().nvfp4_last_error().decode() if rc == -4 else ""
+        raise Nvfp4Error(rc, where, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("nvfp4: tensors must live in GPU memory (no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError("nvfp4: tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype(x: torch.Tensor):
+    if x.dtype == torch.float32:
+        return F32
+    if x.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("nvfp4: input must be float32 or bfloat16")
+
+
+# ---- entry points with the C names (argument marshalling only) ----------
+def nvfp4_quantize(x, rounding, seed, rht, rht_seed, codes, scales, tensor_scale,
+                   codes_t=None, scales_t=None):
+    rows, cols = x.shape
+    _check(lib().nvfp4_quantize(_ptr(x), _dtype(x), rows, cols, int(rounding), int(seed),
+                                int(rht), int(rht_seed), _ptr(codes), _ptr(scales),
+                                _ptr(tensor_scale), _ptr(codes_t), _ptr(scales_t), _stream(x)),
+           "nvfp4_quantize")
+
+
+def nvfp4_quantize_2d(w, rounding, seed, codes, scales, tensor_scale, codes_t=None, scales_t=None):
+    rows, cols = w.shape
+    _check(lib().nvfp4_quantize_2d(_ptr(w), _dtype(w), rows, cols, int(rounding), int(seed),
+                                   _ptr(codes), _ptr(scales), _ptr(tensor_scale), _ptr(codes_t),
+                                   _ptr(scales_t), _stream(w)), "nvfp4_quantize_2d")
+
+
+def nvfp4_rht(x, rht_seed, y):
+    rows, cols = x.shape
+    _check(lib().nvfp4_rht(_ptr(x), _dtype(x), rows, cols, int(rht_seed), _ptr(y), _stream(x)),
+           "nvfp4_rht")
+
+
+def nvfp4_gemm(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, M, N, K, c):
+    _check(lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_codes),
+                            _ptr(b_scales), _ptr(b_tensor_scale), int(M), int(N), int(K), _ptr(c),
+                            _stream(c)), "nvfp4_gemm")
+
+
+# ---- convenience wrappers ---------------------------------------------------
+@dataclass
+class Quantized:
+    """An NVFP4 tensor of rows x cols quantized along cols (+ optional transpose)."""
+    codes: torch.Tensor          # uint8 [rows][cols/2]
+    scales: torch.Tensor         # uint8 [rows][cols/16]
+    tensor_scale: torch.Tensor   # float32 [2] = (S_enc, amax)
+    codes_t: Optional[torch.Tensor] = None   # uint8 [cols][rows/2]
+    scales_t: Optional[torch.Tensor] = None  # uint8 [cols][rows/16]
+
+    @property
+    def shape(self):
+        return (self.codes.shape[0], self.codes.shape[1] * 2)
+
+    def transposed(self) -> "Quantized":
+        if self.codes_t is None:
+            raise ValueError("no transposed copy was produced")
+        return Quantized(self.codes_t, self.scales_t, self.tensor_scale)
+
+
+def _alloc(rows, cols, device, transposed):
+    u8 = dict(dtype=torch.uint8, device=device)
+    q = Quantized(torch.empty(rows, cols // 2, **u8), torch.empty(rows, cols // 16, **u8),
+                  torch.empty(2, dtype=torch.float32, device=device))
+    if transposed:
+        q.codes_t = torch.empty(cols, rows // 2, **u8)
+        q.scales_t = torch.empty(cols, rows // 16, **u8)
+    return q
+
+
+def quantize(x, rounding=RNE, seed=0, rht=False, rht_seed=0, transposed=False) -> Quantized:
+    rows, cols = x.shape
+    q = _alloc(rows, cols, x.device, transposed)
+    nvfp4_quantize(x, rounding, seed, int(rht), rht_seed, q.codes, q.scales, q.tensor_scale,
+                   q.codes_t, q.scales_t)
+    return q
+
+
+def quantize_2d(w, rounding=RNE, seed=0, transposed=True) -> Quantized:
+    rows, cols = w.shape
+    q = _alloc(rows, cols, w.device, transposed)
+    nvfp4_quantize_2d(w, rounding, seed, q.codes, q.scales, q.tensor_scale, q.codes_t, q.scales_t)
+    return q
+
+
+def rht(x, rht_seed=0):
+    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    nvfp4_rht(x, rht_seed, y)
+    return y
+
+
+def gemm(a: Quantized, b: Quantized, out=None):
+    """C = deq(a) . deq(b)^T, fp32 [M][N]."""
+    M, K = a.shape
+    N, K2 = b.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: {K} vs {K2}")
+    c = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=a.codes.device)
+    nvfp4_gemm(a.codes, a.scales, a.tensor_scale, b.codes, b.scales, b.tensor_scale, M, N, K, c)
+    return c

@@ -1,0 +1,156 @@
+// C-ABI entry points of libnvfp4.so (declared in include/nvfp4.h): host-side
+// argument validation, then the kernel launches of quantize.hip and gemm.hip
+// on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/nvfp4.h"
+#include "internal.hpp"
+#include "nvfp4_device.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int set_hip_error(hipError_t e, const char* where) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(e));
+  return NVFP4_ERR_HIP;
+}
+
+// the tiled kernels put 128-row tiles on grid.y (at most 65535)
+constexpr int64_t kMaxTiledRows = INT64_C(65535) * 128;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+// compute-unit count of the current device, cached per device
+int device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_hip_error(e, "hipGetDevice");
+  if (dev >= 0 && dev < kMaxDevices) {
+    int v = g_cus[dev].load(std::memory_order_relaxed);
+    if (v > 0) {
+      *cus = v;
+      return NVFP4_OK;
+    }
+  }
+  int v = 0;
+  e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return set_hip_error(e, "hipDeviceGetAttribute");
+  if (v <= 0) v = 1;
+  if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(v, std::memory_order_relaxed);
+  *cus = v;
+  return NVFP4_OK;
+}
+
+int check_launch(const char* where) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_hip_error(e, where);
+  return NVFP4_OK;
+}
+
+// rows * cols must fit comfortably in int64 arithmetic
+bool size_ok(int64_t rows, int64_t cols) { return rows <= (INT64_C(1) << 40) / cols; }
+
+int validate_quant(const void* x, int dtype, int64_t rows, int64_t cols, int rounding, uint8_t* codes,
+                   uint8_t* scales, float* tensor_scale, uint8_t* codes_t, uint8_t* scales_t) {
+  if (!x || !codes || !scales || !tensor_scale) return NVFP4_ERR_ARG;
+  if (dtype != NVFP4_F32 && dtype != NVFP4_BF16) return NVFP4_ERR_ARG;
+  if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_ARG;
+  if ((codes_t == nullptr) != (scales_t == nullptr)) return NVFP4_ERR_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0 || !size_ok(rows, cols)) return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4)) return NVFP4_ERR_ALIGN;
+  if (codes_t && !aligned(codes_t, 8)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_ARG: return "invalid argument";
+    case NVFP4_ERR_SHAPE: return "invalid shape";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer";
+    case NVFP4_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* nvfp4_last_error(void) { return g_last_error; }
+
+int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int rounding, uint64_t seed,
+                   int rht, uint64_t rht_seed, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                   uint8_t* codes_t, uint8_t* scales_t, void* stream) {
+  int st = validate_quant(x, dtype, rows, cols, rounding, codes, scales, tensor_scale, codes_t, scales_t);
+  if (st) return st;
+  if (rht != 0 && rht != 1) return NVFP4_ERR_ARG;
+  if (codes_t && rht) return NVFP4_ERR_ARG;
+  if (codes_t && rows % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (codes_t && rows > kMaxTiledRows) return NVFP4_ERR_SHAPE;
+  int cus = 0;
+  if ((st = device_cus(&cus))) return st;
+  nvfp4::QuantArgs a{x,      dtype == NVFP4_BF16, rows,   cols,   rounding,     seed,    rht == 1,
+                     rht ? nvfp4::rht_sign_mask(rht_seed) : 0u,  false, codes, scales, tensor_scale,
+                     codes_t, scales_t};
+  nvfp4::launch_quantize(a, cus, (hipStream_t)stream);
+  return check_launch("nvfp4_quantize");
+}
+
+int nvfp4_quantize_2d(const void* w, int dtype, int64_t rows, int64_t cols, int rounding, uint64_t seed,
+                      uint8_t* codes, uint8_t* scales, float* tensor_scale, uint8_t* codes_t,
+                      uint8_t* scales_t, void* stream) {
+  int st = validate_quant(w, dtype, rows, cols, rounding, codes, scales, tensor_scale, codes_t, scales_t);
+  if (st) return st;
+  if (rows % 16 != 0 || rows > kMaxTiledRows) return NVFP4_ERR_SHAPE;
+  int cus = 0;
+  if ((st = device_cus(&cus))) return st;
+  nvfp4::QuantArgs a{w,      dtype == NVFP4_BF16, rows, cols,   rounding,     seed,    false,
+                     0u,     true,                codes, scales, tensor_scale, codes_t, scales_t};
+  nvfp4::launch_quantize(a, cus, (hipStream_t)stream);
+  return check_launch("nvfp4_quantize_2d");
+}
+
+int nvfp4_rht(const void* x, int dtype, int64_t rows, int64_t cols, uint64_t rht_seed, float* y,
+              void* stream) {
+  if (!x || !y) return NVFP4_ERR_ARG;
+  if (dtype != NVFP4_F32 && dtype != NVFP4_BF16) return NVFP4_ERR_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0 || !size_ok(rows, cols)) return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
+  int cus = 0;
+  int st = device_cus(&cus);
+  if (st) return st;
+  nvfp4::launch_rht(x, dtype == NVFP4_BF16, rows, cols, nvfp4::rht_sign_mask(rht_seed), y, cus,
+                    (hipStream_t)stream);
+  return check_launch("nvfp4_rht");
+}
+
+int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+               const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale, int64_t M,
+               int64_t N, int64_t K, float* c, void* stream) {
+  if (!a_codes || !a_scales || !a_tensor_scale || !b_codes || !b_scales || !b_tensor_scale || !c)
+    return NVFP4_ERR_ARG;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!size_ok(M, K) || !size_ok(N, K) || !size_ok(M, N)) return NVFP4_ERR_SHAPE;
+  if (M > INT64_C(65535) * 128) return NVFP4_ERR_SHAPE;  // grid.y limit
+  if (!aligned(a_codes, 8) || !aligned(b_codes, 8) || !aligned(c, 4) || !aligned(a_tensor_scale, 4) ||
+      !aligned(b_tensor_scale, 4))
+    return NVFP4_ERR_ALIGN;
+  int cus = 0;
+  int st = device_cus(&cus);
+  if (st) return st;
+  nvfp4::GemmArgs g{a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, M, N, K, c};
+  nvfp4::launch_gemm(g, cus, (hipStream_t)stream);
+  return check_launch("nvfp4_gemm");
+}
+
+}  // extern "C"

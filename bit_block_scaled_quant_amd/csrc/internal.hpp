@@ -1,0 +1,44 @@
+// Launchers shared by the C-ABI entry points (host side of the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace nvfp4 {
+
+struct QuantArgs {
+  const void* x;
+  bool bf16;
+  int64_t rows, cols;
+  int rounding;  // 0 RNE, 1 SR
+  uint64_t seed;
+  bool rht;
+  uint32_t rht_mask;
+  bool two_d;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* tensor_scale;
+  uint8_t* codes_t;  // may be null
+  uint8_t* scales_t;
+};
+
+void launch_quantize(const QuantArgs& a, int cus, hipStream_t st);
+void launch_rht(const void* x, bool bf16, int64_t rows, int64_t cols, uint32_t mask, float* y, int cus,
+                hipStream_t st);
+
+struct GemmArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_ts;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  const float* b_ts;
+  int64_t M, N, K;
+  float* c;
+};
+
+void launch_gemm(const GemmArgs& g, int cus, hipStream_t st);
+
+}  // namespace nvfp4

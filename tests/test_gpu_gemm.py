@@ -1,0 +1,138 @@
+"""GPU parity of the block-scaled GEMM against the oracle.
+
+Operands are quantized by the oracle (never by the HIP path) from the seeded
+workload tensors, uploaded, multiplied on the GPU, and every output (small
+cases) or a sample of outputs that covers the edges and every tile position
+(full-size cases) must satisfy |C_gpu - C| <= 1e-5 * sum_k |a_ik b_jk| with C
+and the sum computed by the oracle in double."""
+import numpy as np
+import pytest
+import torch
+
+import bit_block_scaled_quant_amd as nv
+import oracle
+from bit_block_scaled_quant_amd import datagen
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = 1e-5
+
+
+def upload(ref):
+    codes, scales, ts = ref[0], ref[1], ref[2]
+    return nv.Quantized(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                        torch.from_numpy(ts).to(DEV))
+
+
+def check_full(c_gpu, ref, refabs):
+    c = c_gpu.detach().cpu().numpy().astype(np.float64)
+    err = np.abs(c - ref)
+    bad = np.argwhere(err > TOL * refabs)
+    assert bad.size == 0, (f"{len(bad)} outputs outside tolerance, first {bad[:4].tolist()}, "
+                           f"worst ratio {np.max(err / np.maximum(refabs, 1e-300))}")
+    return float(np.max(err / np.maximum(refabs, 1e-300)))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (64, 64, 128), (200, 136, 272),
+                                   (130, 250, 512), (1, 1, 16), (17, 300, 48), (129, 129, 1024),
+                                   (384, 128, 4096)])
+def test_gemm_small(M, N, K):
+    a = datagen.tiny(tag=datagen.TAG_A, rows=M, cols=K, seed=M)
+    b = datagen.tiny(tag=datagen.TAG_B, rows=N, cols=K, seed=N)
+    ra = oracle.quantize_1d(a.numpy())
+    rb = oracle.quantize_1d(b.numpy(), rounding=1, seed=3)
+    c = nv.gemm(upload(ra), upload(rb))
+    torch.cuda.synchronize()
+    ref, refabs = oracle.gemm(ra[0], ra[1], ra[2][0], rb[0], rb[1], rb[2][0])
+    check_full(c, ref, refabs)
+
+
+def test_gemm_random_codes_and_scales():
+    rng = np.random.default_rng(0)
+    M, N, K = 160, 96, 640
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    asc = rng.integers(0, 0x7F, (M, K // 16), dtype=np.uint8)
+    bsc = rng.integers(0, 0x7F, (N, K // 16), dtype=np.uint8)
+    ta, tb = np.array([0.37, 1.0], np.float32), np.array([1234.5, 1.0], np.float32)
+    c = nv.gemm(upload((ac, asc, ta)), upload((bc, bsc, tb)))
+    torch.cuda.synchronize()
+    ref, refabs = oracle.gemm(ac, asc, ta[0], bc, bsc, tb[0])
+    check_full(c, ref, refabs)
+
+
+def test_gemm_exact_with_unit_scales():
+    """Scale bytes 0x38 (1.0) and S = 1: every partial sum is a multiple of
+    0.25 below 2^22, so the fp32 result must be exact."""
+    rng = np.random.default_rng(1)
+    M, N, K = 256, 192, 2048
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    ones = lambda r: np.full((r, K // 16), 0x38, np.uint8)
+    t1 = np.array([1.0, 2688.0], np.float32)
+    c = nv.gemm(upload((ac, ones(M), t1)), upload((bc, ones(N), t1)))
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm(ac, ones(M), 1.0, bc, ones(N), 1.0)
+    assert np.array_equal(c.cpu().numpy().astype(np.float64), ref)
+
+
+def test_gemm_symmetry_and_determinism():
+    a = datagen.tiny(tag=datagen.TAG_A, rows=192, cols=512, seed=5)
+    b = datagen.tiny(tag=datagen.TAG_B, rows=320, cols=512, seed=6)
+    qa, qb = upload(oracle.quantize_1d(a.numpy())), upload(oracle.quantize_1d(b.numpy()))
+    c1 = nv.gemm(qa, qb)
+    c2 = nv.gemm(qa, qb)
+    ct = nv.gemm(qb, qa)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    assert torch.allclose(c1, ct.t(), rtol=1e-6, atol=0)
+
+
+def sample_positions(M, N, n=3000, seed=0):
+    rng = np.random.default_rng(seed)
+    ii = [0, M - 1, 0, M - 1]
+    jj = [0, 0, N - 1, N - 1]
+    # full first and last row / column bands, and every position inside a tile
+    for t in range(128):
+        ii += [t % M, (M - 1 - t) % M, int(rng.integers(0, M)), int(rng.integers(0, M))]
+        jj += [int(rng.integers(0, N)), int(rng.integers(0, N)), t % N, (N - 1 - t) % N]
+    ii += list(rng.integers(0, M, n))
+    jj += list(rng.integers(0, N, n))
+    return np.array(ii, np.int64), np.array(jj, np.int64)
+
+
+def gemm_full_case(a_ref, b_ref, M, N, K):
+    c = nv.gemm(upload(a_ref), upload(b_ref))
+    torch.cuda.synchronize()
+    ii, jj = sample_positions(M, N)
+    ref, refabs = oracle.gemm_sample(a_ref[0], a_ref[1], a_ref[2][0], b_ref[0], b_ref[1],
+                                     b_ref[2][0], ii, jj)
+    got = c[torch.from_numpy(ii).to(DEV), torch.from_numpy(jj).to(DEV)].cpu().numpy()
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.all(err <= TOL * refabs), np.max(err / np.maximum(refabs, 1e-300))
+    assert torch.isfinite(c).all()
+
+
+@pytest.mark.timeout(900)
+def test_gemm_full_fprop():
+    x = datagen.act(DEV)
+    w = datagen.weight(DEV)
+    gemm_full_case(oracle.quantize_1d(datagen.bf16_bits(x)),
+                   oracle.quantize_2d(datagen.bf16_bits(w), transposed=False), 8192, 20480, 5120)
+
+
+@pytest.mark.timeout(900)
+def test_gemm_full_dgrad():
+    dy = datagen.grad(DEV)
+    w = datagen.weight(DEV)
+    qw = oracle.quantize_2d(datagen.bf16_bits(w))
+    gemm_full_case(oracle.quantize_1d(datagen.bf16_bits(dy), rounding=1),
+                   (qw[3], qw[4], qw[2]), 8192, 5120, 20480)
+
+
+@pytest.mark.timeout(900)
+def test_gemm_full_wgrad():
+    dyt = datagen.grad(DEV).t().contiguous()
+    xt = datagen.act(DEV).t().contiguous()
+    gemm_full_case(oracle.quantize_1d(datagen.bf16_bits(dyt), rounding=1, rht=1),
+                   oracle.quantize_1d(datagen.bf16_bits(xt), rht=1), 20480, 5120, 8192)
