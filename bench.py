@@ -1,0 +1,279 @@
+"""Benchmark: one NVFP4 training pass of a 12B-class FFN-up linear layer on one
+MI355X, through the C ABI.
+
+A step is the whole hot path over one batch of synthetic input resident in
+HBM (shapes of a 12B hybrid Mamba-Transformer layer, "Pretraining Large
+Language Models with NVFP4", sections 2B and 3):
+  fprop  quantize X [8192x5120] (1D, RNE); quantize W [20480x5120] (2D 16x16,
+         RNE, + transposed copy); Y = X . W^T            (M, N, K = 8192, 20480, 5120)
+  dgrad  quantize dY [8192x20480] (1D, SR); dX = dY . W  (8192, 5120, 20480)
+         using W's transposed copy
+  wgrad  quantize dY^T [20480x8192] (1D, SR, RHT) and X^T [5120x8192] (1D, RNE,
+         RHT); dW = dY^T . X                              (20480, 5120, 8192)
+value = GEMM flops of the step (3 x 2MNK) / wall time of the step, quantizers
+included.  Per-call times come from HIP events on the launch stream.
+
+Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 GEMM TFLOPS + quantize GB/s at 12B-layer shapes (% of roofline)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+FP4_PEAK_TFLOPS = 10100.0       # dense MXFP4 (context only; not usable exactly for NVFP4)
+TOKENS, HIDDEN, FFN = 8192, 5120, 20480
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--seed", type=int, default=0)
+    return p.parse_args()
+
+
+def quant_bytes(rows, cols, in_bytes, transposed):
+    """Algorithmic HBM bytes of one quantize call: the input read twice (amax
+    pass, encode pass) plus codes (1/2 B) and scales (1/16 B) per element for
+    each copy written."""
+    n = rows * cols
+    copies = 2 if transposed else 1
+    return 2 * in_bytes * n + copies * n * (0.5 + 1.0 / 16.0)
+
+
+def gemm_bytes(M, N, K):
+    return (M + N) * K * (0.5 + 1.0 / 16.0) + 4.0 * M * N
+
+
+def traffic_record(kernel_src):
+    """HBM bytes per launch measured by rocprofv3 counters, valid only for the
+    kernel source they were taken with."""
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on a bounded sample of the same step; its
+    per-element / per-output rates are scaled to the full step."""
+    import oracle
+    from bit_block_scaled_quant_amd import datagen
+    t_total = 0.0
+    detail = []
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    rows = 1024
+    x = datagen.bf16_bits(datagen.act(tokens=rows, hidden=HIDDEN))
+    w = datagen.bf16_bits(datagen.weight(out_features=rows, in_features=HIDDEN))
+    dy = datagen.bf16_bits(datagen.grad(tokens=rows // 4, out_features=FFN))
+    dyt = datagen.bf16_bits(datagen.grad(tokens=rows, out_features=TOKENS))
+    xt = datagen.bf16_bits(datagen.act(tokens=rows, hidden=TOKENS))
+    quant_jobs = [
+        ("X 1D RNE", lambda: oracle.quantize_1d(x), x.size, TOKENS * HIDDEN),
+        ("W 2D RNE +T", lambda: oracle.quantize_2d(w), w.size, FFN * HIDDEN),
+        ("dY 1D SR", lambda: oracle.quantize_1d(dy, rounding=1), dy.size, TOKENS * FFN),
+        ("dYt 1D SR RHT", lambda: oracle.quantize_1d(dyt, rounding=1, rht=1), dyt.size,
+         FFN * TOKENS),
+        ("Xt 1D RNE RHT", lambda: oracle.quantize_1d(xt, rht=1), xt.size, HIDDEN * TOKENS),
+    ]
+    for name, fn, n_sample, n_full in quant_jobs:
+        dt = timed(fn)
+        t_total += dt * n_full / n_sample
+        detail.append(f"{name}: {n_sample} of {n_full} elements")
+    qx = oracle.quantize_1d(x)
+    qw = oracle.quantize_1d(w)
+    rng = np.random.default_rng(0)
+    for name, (M, N, K) in (("fprop", (TOKENS, FFN, HIDDEN)), ("dgrad", (TOKENS, HIDDEN, FFN)),
+                            ("wgrad", (FFN, HIDDEN, TOKENS))):
+        # the oracle's cost per output is K multiply-adds; sample at K = 5120
+        s = 4096
+        ii = rng.integers(0, rows, s)
+        jj = rng.integers(0, rows, s)
+        dt = timed(lambda: oracle.gemm_sample(qx[0], qx[1], qx[2][0], qw[0], qw[1], qw[2][0], ii, jj))
+        per_mac = dt / (s * HIDDEN)
+        t_total += per_mac * M * N * K
+        detail.append(f"{name}: {s} outputs x {HIDDEN} MACs")
+    flops = 3 * 2.0 * TOKENS * FFN * HIDDEN
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "; ".join(detail) + f"; extrapolated step time {t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
+              "single-GPU by design, see DESIGN.md for how it would shard", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_block_scaled_quant_amd as nv
+    from bit_block_scaled_quant_amd import build as nvbuild
+    from bit_block_scaled_quant_amd import datagen
+    if not os.path.exists(nv.LIB_PATH):
+        nvbuild.build()
+    nv.lib()
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    seed = args.seed
+    X = datagen.act(dev, seed=seed)
+    W = datagen.weight(dev, seed=seed)
+    dY = datagen.grad(dev, seed=seed)
+    dYt = dY.t().contiguous()
+    Xt = X.t().contiguous()
+    torch.cuda.synchronize()
+
+    def alloc(rows, cols, transposed):
+        u8 = dict(dtype=torch.uint8, device=dev)
+        q = nv.Quantized(torch.empty(rows, cols // 2, **u8), torch.empty(rows, cols // 16, **u8),
+                         torch.empty(2, dtype=torch.float32, device=dev))
+        if transposed:
+            q.codes_t = torch.empty(cols, rows // 2, **u8)
+            q.scales_t = torch.empty(cols, rows // 16, **u8)
+        return q
+
+    qX = alloc(TOKENS, HIDDEN, False)
+    qW = alloc(FFN, HIDDEN, True)
+    qdY = alloc(TOKENS, FFN, False)
+    qdYt = alloc(FFN, TOKENS, False)
+    qXt = alloc(HIDDEN, TOKENS, False)
+    Y = torch.empty(TOKENS, FFN, dtype=torch.float32, device=dev)
+    dX = torch.empty(TOKENS, HIDDEN, dtype=torch.float32, device=dev)
+    dW = torch.empty(FFN, HIDDEN, dtype=torch.float32, device=dev)
+    qWt = nv.Quantized(qW.codes_t, qW.scales_t, qW.tensor_scale)
+
+    calls = [
+        ("quant_X_1d_rne", "quant", lambda: nv.nvfp4_quantize(X, 0, 0, 0, 0, qX.codes, qX.scales,
+                                                              qX.tensor_scale),
+         quant_bytes(TOKENS, HIDDEN, 2, False)),
+        ("quant_W_2d_rne_t", "quant", lambda: nv.nvfp4_quantize_2d(
+            W, 0, 0, qW.codes, qW.scales, qW.tensor_scale, qW.codes_t, qW.scales_t),
+         quant_bytes(FFN, HIDDEN, 2, True)),
+        ("gemm_fprop", "gemm", lambda: nv.gemm(qX, qW, out=Y), (TOKENS, FFN, HIDDEN)),
+        ("quant_dY_1d_sr", "quant", lambda: nv.nvfp4_quantize(dY, 1, seed, 0, 0, qdY.codes,
+                                                              qdY.scales, qdY.tensor_scale),
+         quant_bytes(TOKENS, FFN, 2, False)),
+        ("gemm_dgrad", "gemm", lambda: nv.gemm(qdY, qWt, out=dX), (TOKENS, HIDDEN, FFN)),
+        ("quant_dYt_1d_sr_rht", "quant", lambda: nv.nvfp4_quantize(
+            dYt, 1, seed, 1, seed, qdYt.codes, qdYt.scales, qdYt.tensor_scale),
+         quant_bytes(FFN, TOKENS, 2, False)),
+        ("quant_Xt_1d_rne_rht", "quant", lambda: nv.nvfp4_quantize(
+            Xt, 0, 0, 1, seed, qXt.codes, qXt.scales, qXt.tensor_scale),
+         quant_bytes(HIDDEN, TOKENS, 2, False)),
+        ("gemm_wgrad", "gemm", lambda: nv.gemm(qdYt, qXt, out=dW), (FFN, HIDDEN, TOKENS)),
+    ]
+
+    def step(events=None):
+        for i, (_, _, fn, _) in enumerate(calls):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed steps (no events inside) for the step time
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-call durations with HIP events on the launch stream
+    per_call = {name: [] for name, _, _, _ in calls}
+    for _ in range(args.steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in calls]
+        step(ev)
+        torch.cuda.synchronize()
+        for (name, _, _, _), (a, b) in zip(calls, ev):
+            per_call[name].append(a.elapsed_time(b))
+
+    gemm_flops = 2.0 * TOKENS * FFN * HIDDEN
+    step_flops = 3 * gemm_flops
+    components = {}
+    gemm_ms = []
+    quant_ms_total, quant_bytes_total = 0.0, 0.0
+    for name, kind, _, meta in calls:
+        ms = float(np.mean(per_call[name]))
+        if kind == "gemm":
+            M, N, K = meta
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            gemm_ms.append(ms)
+            components[name] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                                "frac_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+        else:
+            gbs = meta / (ms * 1e-3) / 1e9
+            quant_ms_total += ms
+            quant_bytes_total += meta
+            components[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
+                                "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    avg_gemm_ms = float(np.mean(gemm_ms))
+    achieved = gemm_flops / (avg_gemm_ms * 1e-3) / 1e12
+    rec = traffic_record(os.path.join(ROOT, "bit_block_scaled_quant_amd", "csrc", "gemm.hip"))
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
+                "traffic": (rec["bytes_per_launch"] if rec else None),
+                "kernel": "k_gemm (fp16 MFMA 16x16x32, fp32 accumulate)",
+                "algorithmic_flops_per_launch": gemm_flops,
+                "context_frac_of_fp4_peak": round(achieved / FP4_PEAK_TFLOPS, 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 operands, fp16 MFMA, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "12B FFN-up linear layer, NVFP4 fprop+dgrad+wgrad",
+                   "X": [TOKENS, HIDDEN], "W": [FFN, HIDDEN], "dY": [TOKENS, FFN],
+                   "gemm_MNK": [[TOKENS, FFN, HIDDEN], [TOKENS, HIDDEN, FFN],
+                                [FFN, HIDDEN, TOKENS]]},
+        "gemm_TFLOPs": round(achieved, 1),
+        "quantize_GBps": round(quant_bytes_total / (quant_ms_total * 1e-3) / 1e9, 1),
+        "quantize_frac_hbm_peak": round(quant_bytes_total / (quant_ms_total * 1e-3) / 1e9
+                                        / HBM_PEAK_GBS, 4),
+        "components": components,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
