@@ -16,11 +16,12 @@
 // applied once in the epilogue.  (gfx950's scaled FP4 MFMA takes power-of-two
 // scales per 32 elements, which cannot represent E4M3 scales per 16.)
 //
-// Tiling: a 256-thread workgroup owns a 128x128 tile of C and walks K in
+// Tiling: a 256-thread workgroup owns a 256x256 tile of C and walks K in
 // steps of 128.  Packed codes and scale bytes are staged through LDS (double
 // buffered, 16-byte chunks XOR-swizzled against bank conflicts); each wave
-// owns a 64x64 sub-tile, reads its packed fragments from LDS and expands
-// them in registers.  Lane group g = lane / 16 of a fragment covers the 32
+// owns a 128x128 sub-tile (accumulators in AGPRs), reads its packed
+// fragments from LDS and expands them in registers: per 128x128x32 of MFMA
+// work a lane converts 64 elements, which hides under the matrix cores.  Lane group g = lane / 16 of a fragment covers the 32
 // K-elements [32g, 32g+32) of a step; its word s feeds MFMA slice s.  A and B
 // use the same lane-to-K map, so the products pair up correctly.
 #include "internal.hpp"
@@ -32,17 +33,17 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGemmThreads = 256;
-constexpr int kBM = 128, kBN = 128;
+constexpr int kGemmThreads = 256;  // 4 waves in a 2 x 2 grid
 constexpr int kBK = 128;           // K-elements per step
 constexpr int kRowBytes = kBK / 2;  // 64 bytes of codes per row per step
 constexpr int kRowScales = kBK / 16;
 
+template <int BM, int BN>
 struct __align__(16) GemmStage {
-  uint8_t a[kBM * kRowBytes];
-  uint8_t b[kBN * kRowBytes];
-  uint8_t as[kBM * kRowScales];
-  uint8_t bs[kBN * kRowScales];
+  uint8_t a[BM * kRowBytes];
+  uint8_t b[BN * kRowBytes];
+  uint8_t as[BM * kRowScales];
+  uint8_t bs[BN * kRowScales];
 };
 
 // 16-byte chunk c of row r lives at chunk c ^ ((r >> 1) & 3): eight
@@ -50,46 +51,27 @@ struct __align__(16) GemmStage {
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ ((r >> 1) & 3)) << 4); }
 
 // Eight E2M1 codes (element 2k in the low nibble of byte k) -> eight exact
-// fp16 values times the block scale, in the lane order
-// [n0, n4, n1, n5, n2, n6, n3, n7].  Magnitudes come from a byte table via
-// v_perm (fp16 high bytes of 0, .5, 1, 1.5, 2, 3, 4, 6; low bytes are 0),
-// the sign bit is moved into place, and one packed multiply applies the
-// scale (exact: at most 6 significant bits).
+// fp16 values times the block scale, in element order.  The gfx950
+// conversion v_cvt_scalef32_pk_f16_fp4 turns one byte into two fp16 values
+// times a power-of-two scale exactly (checked for all 256 bytes); here the
+// scale is 2^8.  The E4M3 scale byte b enters as the fp16 whose bits are
+// (b & 0x7F) << 7, which is its value times 2^-8 (subnormal E4M3 bytes become
+// fp16 subnormals), so one packed multiply yields code * scale exactly: the
+// product has at most 6 significant bits and lies in [2^-10, 2688].
 __device__ __forceinline__ half8 unpack8(uint32_t w, half2v sc) {
-  const uint32_t lo = w & 0x07070707u;         // n0 n2 n4 n6
-  const uint32_t hi = (w >> 4) & 0x07070707u;  // n1 n3 n5 n7
-  const uint32_t z = 0x0C0C0C0Cu;              // selector 0x0C yields 0x00
-  const uint32_t tlo = 0x3E3C3800u, thi = 0x46444240u;
-  const uint32_t s0 = __builtin_amdgcn_perm(z, lo, 0x02040004u);  // [0C n0 0C n4]
-  const uint32_t s1 = __builtin_amdgcn_perm(z, hi, 0x02040004u);  // [0C n1 0C n5]
-  const uint32_t s2 = __builtin_amdgcn_perm(z, lo, 0x03040104u);  // [0C n2 0C n6]
-  const uint32_t s3 = __builtin_amdgcn_perm(z, hi, 0x03040104u);  // [0C n3 0C n7]
-  uint32_t d[4];
-  d[0] = __builtin_amdgcn_perm(thi, tlo, s0) | ((w << 12) & 0x80008000u);
-  d[1] = __builtin_amdgcn_perm(thi, tlo, s1) | ((w << 8) & 0x80008000u);
-  d[2] = __builtin_amdgcn_perm(thi, tlo, s2) | ((w << 4) & 0x80008000u);
-  d[3] = __builtin_amdgcn_perm(thi, tlo, s3) | (w & 0x80008000u);
-  half8 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    half2v p = __builtin_bit_cast(half2v, d[i]) * sc;
-    out[2 * i] = p[0];
-    out[2 * i + 1] = p[1];
-  }
-  return out;
+  const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * sc;
+  const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * sc;
+  const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * sc;
+  const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * sc;
+  return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// E4M3 byte -> (scale * 2^-8, scale * 2^-8) as packed fp16 bits
 __device__ __forceinline__ half2v scale_h2(uint32_t byte) {
-  const _Float16 h = (_Float16)e4m3_decode(byte);  // exact: 2^-9 .. 448
-  return half2v{h, h};
+  return __builtin_bit_cast(half2v, (byte & 0x7Fu) * 0x00800080u);
 }
 
 // ---- global -> registers -> LDS -----------------------------------------
-struct Staged {
-  uint4 a[2], b[2];
-  uint2 s;  // threads 0..127: 8 A scale bytes of a row; 128..255: B
-};
-
 template <bool ALIGNED>
 __device__ __forceinline__ uint4 load_chunk(const uint8_t* __restrict__ codes, int64_t row, int64_t K,
                                             int64_t kk) {
@@ -106,6 +88,7 @@ __device__ __forceinline__ uint4 load_chunk(const uint8_t* __restrict__ codes, i
   return v;
 }
 
+// the 8 scale bytes of one row for K-elements [k0, k0 + 128)
 template <bool ALIGNED>
 __device__ __forceinline__ uint2 load_scales(const uint8_t* __restrict__ scales, int64_t row, int64_t K,
                                              int64_t k0) {
@@ -117,107 +100,161 @@ __device__ __forceinline__ uint2 load_scales(const uint8_t* __restrict__ scales,
   return make_uint2(w[0], w[1]);
 }
 
-template <bool ALIGNED>
+template <int BM, int BN>
+struct Staged {
+  static constexpr int kA = BM * 4 / kGemmThreads, kB = BN * 4 / kGemmThreads;
+  static constexpr int kS = (BM + BN) / kGemmThreads;  // scale rows per thread
+  uint4 a[kA], b[kB];
+  uint2 s[kS];
+};
+
+template <int BM, int BN, bool ALIGNED>
 __device__ __forceinline__ void stage_load(const GemmArgs& g, int64_t m0, int64_t n0, int64_t k0,
-                                           Staged& st) {
+                                           Staged<BM, BN>& st) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < Staged<BM, BN>::kA; ++i) {
     const int idx = t + i * kGemmThreads;
     const int row = idx >> 2, chunk = idx & 3;
     const int64_t kk = k0 + chunk * 32;
-    const int64_t ra = min(m0 + row, g.M - 1), rb = min(n0 + row, g.N - 1);
-    st.a[i] = (ALIGNED || kk < g.K) ? load_chunk<ALIGNED>(g.a_codes, ra, g.K, kk) : make_uint4(0, 0, 0, 0);
-    st.b[i] = (ALIGNED || kk < g.K) ? load_chunk<ALIGNED>(g.b_codes, rb, g.K, kk) : make_uint4(0, 0, 0, 0);
+    st.a[i] = (ALIGNED || kk < g.K) ? load_chunk<ALIGNED>(g.a_codes, min(m0 + row, g.M - 1), g.K, kk)
+                                    : make_uint4(0, 0, 0, 0);
   }
-  if (t < kBM)
-    st.s = load_scales<ALIGNED>(g.a_scales, min(m0 + t, g.M - 1), g.K, k0);
-  else
-    st.s = load_scales<ALIGNED>(g.b_scales, min(n0 + t - kBM, g.N - 1), g.K, k0);
-}
-
-__device__ __forceinline__ void stage_store(GemmStage& sm, const Staged& st) {
-  const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < Staged<BM, BN>::kB; ++i) {
     const int idx = t + i * kGemmThreads;
     const int row = idx >> 2, chunk = idx & 3;
-    *reinterpret_cast<uint4*>(sm.a + swz(row, chunk)) = st.a[i];
-    *reinterpret_cast<uint4*>(sm.b + swz(row, chunk)) = st.b[i];
+    const int64_t kk = k0 + chunk * 32;
+    st.b[i] = (ALIGNED || kk < g.K) ? load_chunk<ALIGNED>(g.b_codes, min(n0 + row, g.N - 1), g.K, kk)
+                                    : make_uint4(0, 0, 0, 0);
   }
-  if (t < kBM)
-    *reinterpret_cast<uint2*>(sm.as + t * kRowScales) = st.s;
-  else
-    *reinterpret_cast<uint2*>(sm.bs + (t - kBM) * kRowScales) = st.s;
+#pragma unroll
+  for (int i = 0; i < Staged<BM, BN>::kS; ++i) {
+    const int r = t + i * kGemmThreads;  // rows 0..BM-1 of A, then BN rows of B
+    if (r < BM)
+      st.s[i] = load_scales<ALIGNED>(g.a_scales, min(m0 + r, g.M - 1), g.K, k0);
+    else
+      st.s[i] = load_scales<ALIGNED>(g.b_scales, min(n0 + r - BM, g.N - 1), g.K, k0);
+  }
+}
+
+// LDS position of scale byte (row r, block column c) of a BM-row operand:
+// column-major over the 8 block columns, and inside a column the rows of
+// each wave half ordered (lane row li, tile i), so that a lane reads the
+// scales of all its tiles for one column with a single 8-byte load.
+template <int BM>
+__device__ __forceinline__ int scale_pos(int r, int c) {
+  constexpr int TI = BM / 32;
+  return c * BM + (r / (BM / 2)) * (BM / 2) + (r & 15) * TI + ((r % (BM / 2)) >> 4);
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void stage_store(GemmStage<BM, BN>& sm, const Staged<BM, BN>& st) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < Staged<BM, BN>::kA; ++i) {
+    const int idx = t + i * kGemmThreads;
+    *reinterpret_cast<uint4*>(sm.a + swz(idx >> 2, idx & 3)) = st.a[i];
+  }
+#pragma unroll
+  for (int i = 0; i < Staged<BM, BN>::kB; ++i) {
+    const int idx = t + i * kGemmThreads;
+    *reinterpret_cast<uint4*>(sm.b + swz(idx >> 2, idx & 3)) = st.b[i];
+  }
+#pragma unroll
+  for (int i = 0; i < Staged<BM, BN>::kS; ++i) {
+    const int r = t + i * kGemmThreads;
+    const uint32_t w[2] = {st.s[i].x, st.s[i].y};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint8_t v = (uint8_t)(w[c >> 2] >> (8 * (c & 3)));
+      if (r < BM)
+        sm.as[scale_pos<BM>(r, c)] = v;
+      else
+        sm.bs[scale_pos<BN>(r - BM, c)] = v;
+    }
+  }
 }
 
 // ---- the kernel ---------------------------------------------------------
-template <bool ALIGNED>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs g) {
-  __shared__ GemmStage smem[2];
-  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+// BM x BN tile per workgroup, (BM/2) x (BN/2) per wave.
+template <int BM, int BN, bool ALIGNED>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
+  constexpr int TI = BM / 32, TJ = BN / 32;  // 16x16 MFMA tiles per wave
+  __shared__ GemmStage<BM, BN> smem[2];
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 15, lg = lane >> 4;
 
-  floatx4 acc[4][4];
+  floatx4 acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int64_t nk = (g.K + kBK - 1) / kBK;
-  Staged st;
-  stage_load<ALIGNED>(g, m0, n0, 0, st);
-  stage_store(smem[0], st);
+  Staged<BM, BN> st;
+  stage_load<BM, BN, ALIGNED>(g, m0, n0, 0, st);
+  stage_store<BM, BN>(smem[0], st);
   __syncthreads();
 
   for (int64_t kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
-    if (more) stage_load<ALIGNED>(g, m0, n0, (kt + 1) * kBK, st);
-    const GemmStage& sm = smem[kt & 1];
+    if (more) stage_load<BM, BN, ALIGNED>(g, m0, n0, (kt + 1) * kBK, st);
+    const GemmStage<BM, BN>& sm = smem[kt & 1];
 
-    uint4 qa[4], qb[4];
-    uint32_t sa[4], sb[4];
+    // two halves of the step: words 2h, 2h+1 of each fragment share the
+    // scale byte h (K-elements 32g + 16h .. 32g + 16h + 15)
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+      uint2 qa[TI], qb[TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 64 + i * 16 + li, rb = wn * 64 + i * 16 + li;
-      qa[i] = *reinterpret_cast<const uint4*>(sm.a + swz(ra, lg));
-      qb[i] = *reinterpret_cast<const uint4*>(sm.b + swz(rb, lg));
-      sa[i] = *reinterpret_cast<const uint16_t*>(sm.as + ra * kRowScales + 2 * lg);
-      sb[i] = *reinterpret_cast<const uint16_t*>(sm.bs + rb * kRowScales + 2 * lg);
-    }
+      for (int i = 0; i < TI; ++i)
+        qa[i] = *reinterpret_cast<const uint2*>(sm.a + swz(wm * (BM / 2) + i * 16 + li, lg) + 8 * h);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      half8 fa[4], fb[4];
+      for (int j = 0; j < TJ; ++j)
+        qb[j] = *reinterpret_cast<const uint2*>(sm.b + swz(wn * (BN / 2) + j * 16 + li, lg) + 8 * h);
+      // scale bytes of block column 2g + h for all tiles of this lane
+      const uint8_t* pa = sm.as + (2 * lg + h) * BM + wm * (BM / 2) + li * TI;
+      const uint8_t* pb = sm.bs + (2 * lg + h) * BN + wn * (BN / 2) + li * TJ;
+      uint8_t ba[TI], bb[TJ];
+      *reinterpret_cast<uint2*>(ba) = *reinterpret_cast<const uint2*>(pa);
+      *reinterpret_cast<uint2*>(bb) = *reinterpret_cast<const uint2*>(pb);
+      half2v sa[TI], sb[TJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t wa = s == 0 ? qa[i].x : s == 1 ? qa[i].y : s == 2 ? qa[i].z : qa[i].w;
-        const uint32_t wb = s == 0 ? qb[i].x : s == 1 ? qb[i].y : s == 2 ? qb[i].z : qb[i].w;
-        fa[i] = unpack8(wa, scale_h2((sa[i] >> (8 * (s >> 1))) & 0xFFu));
-        fb[i] = unpack8(wb, scale_h2((sb[i] >> (8 * (s >> 1))) & 0xFFu));
+      for (int i = 0; i < TI; ++i) sa[i] = scale_h2(ba[i]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) sb[j] = scale_h2(bb[j]);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        half8 fa[TI], fb[TJ];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) fa[i] = unpack8(s ? qa[i].y : qa[i].x, sa[i]);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) fb[j] = unpack8(s ? qb[j].y : qb[j].x, sb[j]);
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (more) stage_store(smem[(kt + 1) & 1], st);
+    if (more) stage_store<BM, BN>(smem[(kt + 1) & 1], st);
     __syncthreads();
   }
 
   // epilogue: C = acc / (S_a * S_b), lane holds rows 4*lg .. 4*lg+3 of column li
   const float inv_a = __fdiv_rn(1.0f, g.a_ts[0]), inv_b = __fdiv_rn(1.0f, g.b_ts[0]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TI; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 16 + li;
+    for (int j = 0; j < TJ; ++j) {
+      const int64_t n = n0 + wn * (BN / 2) + j * 16 + li;
       if (n >= g.N) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm * 64 + i * 16 + lg * 4 + r;
+        const int64_t m = m0 + wm * (BM / 2) + i * 16 + lg * 4 + r;
         if (m < g.M) g.c[m * g.N + n] = (acc[i][j][r] * inv_a) * inv_b;
       }
     }
@@ -226,14 +263,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs g) {
 
 void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
   (void)cus;
-  const dim3 grid((unsigned)((g.N + kBN - 1) / kBN), (unsigned)((g.M + kBM - 1) / kBM));
+  constexpr int BM = 256, BN = 256;
+  const dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM));
   const bool aligned = g.K % kBK == 0 && ((uintptr_t)g.a_codes % 16 == 0) &&
                        ((uintptr_t)g.b_codes % 16 == 0) && ((uintptr_t)g.a_scales % 8 == 0) &&
                        ((uintptr_t)g.b_scales % 8 == 0);
   if (aligned)
-    hipLaunchKernelGGL(k_gemm<true>, grid, dim3(kGemmThreads), 0, st, g);
+    hipLaunchKernelGGL((k_gemm<BM, BN, true>), grid, dim3(kGemmThreads), 0, st, g);
   else
-    hipLaunchKernelGGL(k_gemm<false>, grid, dim3(kGemmThreads), 0, st, g);
+    hipLaunchKernelGGL((k_gemm<BM, BN, false>), grid, dim3(kGemmThreads), 0, st, g);
 }
 
 }  // namespace nvfp4
