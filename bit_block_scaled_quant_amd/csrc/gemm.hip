@@ -261,6 +261,168 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   }
 }
 
+// ---- fast path: direct-to-LDS stages of 256 K-elements -----------------
+// For M, N multiples of 256, K a multiple of 512 and aligned operands.
+// Same 256x256 tile, 128x128 per wave and exact unpack as k_gemm, but
+//  - a stage holds 256 K-elements (128 code bytes and 16 scale bytes per
+//    row), halving the barriers per K;
+//  - operand bytes go from global memory straight into LDS
+//    (global_load_lds_dwordx4 for codes, _dword for scales): no staging
+//    registers and no LDS store instructions;
+//  - in quarter h of a stage, lane group g of a fragment reads one whole
+//    NVFP4 block (K-elements 64g + 16h .. 64g + 16h + 15), so each lane needs
+//    one scale per tile and quarter; scales sit in LDS as four dword planes
+//    per operand, rows in (wave half, lane row, tile) order, and a lane reads
+//    the scales of all its tiles for the whole stage with two 16-byte reads.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+constexpr int kDirBK = 256;                     // K-elements per stage
+constexpr int kDirRow = kDirBK / 2;             // 128 code bytes per row
+constexpr int kDirCodes = 256 * kDirRow;        // 32 KB per operand
+constexpr int kDirScales = 256 * (kDirBK / 16);  // 4 KB per operand
+constexpr int kDirOffB = kDirCodes;
+constexpr int kDirOffAS = 2 * kDirCodes;
+constexpr int kDirOffBS = kDirOffAS + kDirScales;
+constexpr int kDirStage = kDirOffBS + kDirScales;  // 72 KB
+
+// physical 16-byte chunk of logical chunk c in row r (8 chunks per row)
+__device__ __forceinline__ int dswz(int r, int c) { return r * kDirRow + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
+
+// Direct loads of one stage (K-elements [k0, k0 + 256)) into buf.
+// Codes: 1 KB block blk = 8 * wave + u holds rows 8 * blk .. 8 * blk + 7;
+// lane l writes the 16-byte slot 64 * blk + l, i.e. row 8 * blk + l / 8 at
+// physical chunk l % 8, and fetches the logical chunk stored there.
+// Scales: dword slot 128 * wave + 64 * v + l (4 per wave... see below) holds
+// bytes 4p .. 4p + 3 (block columns 4p .. 4p + 3) of one row.
+__device__ __forceinline__ void dir_issue(const GemmArgs& g, int64_t m0, int64_t n0, int64_t k0,
+                                          uint8_t* buf) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t kb = g.K / 2, ks = g.K / 16;
+  const uint8_t* a0 = g.a_codes + m0 * kb + k0 / 2;
+  const uint8_t* b0 = g.b_codes + n0 * kb + k0 / 2;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int blk = 8 * wave + u;
+    const int row = 8 * blk + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    const uint32_t off = (uint32_t)(row * kb + 16 * chunk);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(a0 + off), (lds_void_t*)(buf + 1024 * blk), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(b0 + off), (lds_void_t*)(buf + kDirOffB + 1024 * blk),
+                                     16, 0, 0);
+  }
+  // 1024 dword slots per operand: slot = 256 * plane + q, q = 128 * half +
+  // 8 * li + i for row 128 * half + 16 * i + li; wave w covers slots
+  // 256 * w .. 256 * w + 255 (plane w) in four 64-slot pieces
+  const uint8_t* as0 = g.a_scales + m0 * ks + k0 / 16 + 4 * wave;
+  const uint8_t* bs0 = g.b_scales + n0 * ks + k0 / 16 + 4 * wave;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int q = 64 * v + lane;
+    const int r = 128 * (q >> 7) + 16 * (q & 7) + ((q >> 3) & 15);
+    const uint32_t off = (uint32_t)(r * ks);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(as0 + off),
+                                     (lds_void_t*)(buf + kDirOffAS + 1024 * wave + 256 * v), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(bs0 + off),
+                                     (lds_void_t*)(buf + kDirOffBS + 1024 * wave + 256 * v), 4, 0, 0);
+  }
+}
+
+// one stage of MFMA work from buf: four quarters, each one NVFP4 block per
+// lane group (two MFMA slices)
+__device__ __forceinline__ void dir_compute(const uint8_t* buf, floatx4 (&acc)[8][8], int wm, int wn,
+                                            int li, int lg) {
+  // scale dwords of plane lg (block columns 4g .. 4g + 3) for all tiles
+  uint32_t da[8], db[8];
+  {
+    const uint4* pa = reinterpret_cast<const uint4*>(buf + kDirOffAS + 4 * (lg * 256 + wm * 128 + li * 8));
+    const uint4* pb = reinterpret_cast<const uint4*>(buf + kDirOffBS + 4 * (lg * 256 + wn * 128 + li * 8));
+    const uint4 x0 = pa[0], x1 = pa[1], y0 = pb[0], y1 = pb[1];
+    da[0] = x0.x; da[1] = x0.y; da[2] = x0.z; da[3] = x0.w;
+    da[4] = x1.x; da[5] = x1.y; da[6] = x1.z; da[7] = x1.w;
+    db[0] = y0.x; db[1] = y0.y; db[2] = y0.z; db[3] = y0.w;
+    db[4] = y1.x; db[5] = y1.y; db[6] = y1.z; db[7] = y1.w;
+  }
+#pragma unroll 1
+  for (int h = 0; h < 4; ++h) {
+    // block 4g + h: 8 bytes at logical chunk 2g + h / 2, byte 8 * (h & 1)
+    const int c = 2 * lg + (h >> 1), sub = 8 * (h & 1), sh = 8 * h;
+    uint2 qa[8], qb[8];
+    half2v sa[8], sb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qa[i] = *reinterpret_cast<const uint2*>(buf + dswz(wm * 128 + i * 16 + li, c) + sub);
+      sa[i] = scale_h2(da[i] >> sh);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qb[j] = *reinterpret_cast<const uint2*>(buf + kDirOffB + dswz(wn * 128 + j * 16 + li, c) + sub);
+      sb[j] = scale_h2(db[j] >> sh);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      half8 fa[8], fb[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fa[i] = unpack8(s ? qa[i].y : qa[i].x, sa[i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fb[j] = unpack8(s ? qb[j].y : qb[j].x, sb[j]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_direct(GemmArgs g) {
+  __shared__ __align__(16) uint8_t buf0[kDirStage];
+  __shared__ __align__(16) uint8_t buf1[kDirStage];
+  const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * 256;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 15, lg = lane >> 4;
+
+  floatx4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t nk = g.K / kDirBK;  // even
+  dir_issue(g, m0, n0, 0, buf0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt(0) only
+  __syncthreads();
+  // Unrolled over the two buffers: a stage is computed from one buffer while
+  // the next stage streams into the other; the barrier after each stage
+  // publishes the streamed stage and frees the buffer just read.
+  for (int64_t kt = 0; kt < nk; kt += 2) {
+    dir_issue(g, m0, n0, (kt + 1) * kDirBK, buf1);
+    dir_compute(buf0, acc, wm, wn, li, lg);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __syncthreads();
+    if (kt + 2 < nk) dir_issue(g, m0, n0, (kt + 2) * kDirBK, buf0);
+    dir_compute(buf1, acc, wm, wn, li, lg);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __syncthreads();
+  }
+
+  const float inv_a = __fdiv_rn(1.0f, g.a_ts[0]), inv_b = __fdiv_rn(1.0f, g.b_ts[0]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t n = n0 + wn * 128 + j * 16 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm * 128 + i * 16 + lg * 4 + r;
+        g.c[m * g.N + n] = (acc[i][j][r] * inv_a) * inv_b;
+      }
+    }
+  }
+}
+
 void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
   (void)cus;
   constexpr int BM = 256, BN = 256;
@@ -268,7 +430,10 @@ void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
   const bool aligned = g.K % kBK == 0 && ((uintptr_t)g.a_codes % 16 == 0) &&
                        ((uintptr_t)g.b_codes % 16 == 0) && ((uintptr_t)g.a_scales % 8 == 0) &&
                        ((uintptr_t)g.b_scales % 8 == 0);
-  if (aligned)
+  if (aligned && g.M % 256 == 0 && g.N % 256 == 0 && g.K % (2 * kDirBK) == 0 &&
+      g.K <= (INT64_C(1) << 26) && (uintptr_t)g.a_scales % 4 == 0 && (uintptr_t)g.b_scales % 4 == 0)
+    hipLaunchKernelGGL(k_gemm_direct, grid, dim3(kGemmThreads), 0, st, g);
+  else if (aligned)
     hipLaunchKernelGGL((k_gemm<BM, BN, true>), grid, dim3(kGemmThreads), 0, st, g);
   else
     hipLaunchKernelGGL((k_gemm<BM, BN, false>), grid, dim3(kGemmThreads), 0, st, g);

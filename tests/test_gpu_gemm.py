@@ -35,7 +35,8 @@ def check_full(c_gpu, ref, refabs):
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (64, 64, 128), (200, 136, 272),
                                    (130, 250, 512), (1, 1, 16), (17, 300, 48), (129, 129, 1024),
-                                   (384, 128, 4096)])
+                                   (384, 128, 4096), (256, 256, 512), (512, 768, 1024),
+                                   (768, 256, 3072)])
 def test_gemm_small(M, N, K):
     a = datagen.tiny(tag=datagen.TAG_A, rows=M, cols=K, seed=M)
     b = datagen.tiny(tag=datagen.TAG_B, rows=N, cols=K, seed=N)
@@ -49,7 +50,7 @@ def test_gemm_small(M, N, K):
 
 def test_gemm_random_codes_and_scales():
     rng = np.random.default_rng(0)
-    M, N, K = 160, 96, 640
+    M, N, K = 256, 512, 1536
     ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
     bc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
     asc = rng.integers(0, 0x7F, (M, K // 16), dtype=np.uint8)
@@ -61,11 +62,11 @@ def test_gemm_random_codes_and_scales():
     check_full(c, ref, refabs)
 
 
-def test_gemm_exact_with_unit_scales():
+@pytest.mark.parametrize("M,N,K", [(256, 192, 2048), (512, 256, 2048)])
+def test_gemm_exact_with_unit_scales(M, N, K):
     """Scale bytes 0x38 (1.0) and S = 1: every partial sum is a multiple of
     0.25 below 2^22, so the fp32 result must be exact."""
     rng = np.random.default_rng(1)
-    M, N, K = 256, 192, 2048
     ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
     bc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
     ones = lambda r: np.full((r, K // 16), 0x38, np.uint8)
