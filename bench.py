@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 256 MiB device copy three times (for scaling the "
+                        "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
 
 
@@ -128,6 +131,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": a.numel() * 4, "repeats": 3}), flush=True)
+        return
 
     import bit_block_scaled_quant_amd as nv
     from bit_block_scaled_quant_amd import build as nvbuild
@@ -242,7 +255,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
                 "traffic": (rec["bytes_per_launch"] if rec else None),
-                "kernel": "k_gemm (fp16 MFMA 16x16x32, fp32 accumulate)",
+                "kernel": "k_gemm_direct (fp16 MFMA 16x16x32, fp32 accumulate)",
                 "algorithmic_flops_per_launch": gemm_flops,
                 "context_frac_of_fp4_peak": round(achieved / FP4_PEAK_TFLOPS, 4)}
 
