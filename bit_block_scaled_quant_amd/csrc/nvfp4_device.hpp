@@ -200,6 +200,20 @@ __device__ __forceinline__ float amax16(const float v[16]) {
   return m;
 }
 
+// Round-to-nearest-even of eight values with the gfx950 conversion
+// v_cvt_scalef32_pk_fp4_f32 (scale 1.0: no scaling), two values per
+// instruction, even element in the low nibble of each byte.  Its rounding
+// equals e2m1_rne above for every fp32 input (ties to even, saturation at 6,
+// sign kept); the exhaustive device test checks that against the oracle.
+__device__ __forceinline__ uint32_t e2m1_rne8(const float* y) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+  return w;
+}
+
 // encode 16 elements of one block; codes packed two per byte, even element
 // in the low nibble, into two 32-bit words
 template <bool SR>
@@ -214,10 +228,11 @@ __device__ __forceinline__ uint2 encode16(const float v[16], float inv, uint64_t
 #pragma unroll
     for (int j = 0; j < 8; ++j) hi |= e2m1_sr(v[8 + j] * inv, draw16(p1, j)) << (4 * j);
   } else {
+    float y[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) lo |= e2m1_rne(v[j] * inv) << (4 * j);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) hi |= e2m1_rne(v[8 + j] * inv) << (4 * j);
+    for (int j = 0; j < 16; ++j) y[j] = v[j] * inv;
+    lo = e2m1_rne8(y);
+    hi = e2m1_rne8(y + 8);
   }
   return make_uint2(lo, hi);
 }

@@ -3,10 +3,11 @@
 // "Pretraining Large Language Models with NVFP4", Technische samenvatting,
 // 2A: the FP32 per-tensor scale needs the amax of the whole tensor before any
 // block can be encoded, so a quantization is two passes over the input:
-//   pass 1  k_amax: every thread reduces |x| (after the Hadamard transform of
-//           2B.2 when it is on) over its elements, waves reduce with
-//           cross-lane shuffles, one atomic max per workgroup on the float
-//           bits (non-negative floats order like their bit patterns);
+//   pass 1  k_amax_plain / k_amax_rht: every thread reduces |x| (after the
+//           Hadamard transform of 2B.2 when it is on) over its elements,
+//           waves reduce with cross-lane shuffles, one atomic max per
+//           workgroup on the float bits (non-negative floats order like
+//           their bit patterns);
 //   pass 2  encode: the per-tensor scale is derived from the amax by every
 //           workgroup; each 16-element block gets its E4M3 scale and E2M1
 //           codes (RNE, or SR of 2B.4 with Philox draws).
@@ -35,17 +36,26 @@ __global__ void k_init_amax(float* ts) {
   ts[1] = 0.0f;
 }
 
-template <bool BF16, bool RHT>
-__global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, int64_t nchunks,
-                                                   uint32_t rht_mask, float* __restrict__ ts) {
-  float m = 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += stride) {
-    float v[16];
-    load16<BF16>(x, c * 16, v);
-    if (RHT) rht16(v, rht_mask);
-    m = fmaxf(m, amax16(v));
+// |x| of the two bf16 in a word as the high halves of fp32 bit patterns is
+// order-preserving, so the amax without the transform is an integer max of
+// (w & 0x7FFF7FFF) per 16-bit half (v_pk_max_u16), and of (w & 0x7FFFFFFF)
+// for fp32; four independent 16-byte loads per lane keep enough bytes in
+// flight.
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+
+template <bool BF16>
+__device__ __forceinline__ void absmax_vec(const uint4& q, ushort2v& m16, uint32_t& m32) {
+  if (BF16) {
+    m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2v, q.x & 0x7FFF7FFFu));
+    m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2v, q.y & 0x7FFF7FFFu));
+    m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2v, q.z & 0x7FFF7FFFu));
+    m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2v, q.w & 0x7FFF7FFFu));
+  } else {
+    m32 = max(m32, max(max(q.x & 0x7FFFFFFFu, q.y & 0x7FFFFFFFu), max(q.z & 0x7FFFFFFFu, q.w & 0x7FFFFFFFu)));
   }
+}
+
+__device__ __forceinline__ void block_max_to(float m, float* ts) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   __shared__ float red[kThreads / 64];
@@ -55,6 +65,50 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, i
     for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
     atomicMax(reinterpret_cast<unsigned int*>(ts + 1), __float_as_uint(m));
   }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_amax_plain(const uint4* __restrict__ x, int64_t nvec,
+                                                         float* __restrict__ ts) {
+  ushort2v m16 = {0, 0};
+  uint32_t m32 = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    const uint4 a = x[i], b = x[i + stride], c = x[i + 2 * stride], d = x[i + 3 * stride];
+    absmax_vec<BF16>(a, m16, m32);
+    absmax_vec<BF16>(b, m16, m32);
+    absmax_vec<BF16>(c, m16, m32);
+    absmax_vec<BF16>(d, m16, m32);
+  }
+  for (; i < nvec; i += stride) absmax_vec<BF16>(x[i], m16, m32);
+  const uint32_t bits = BF16 ? ((uint32_t)max(m16.x, m16.y) << 16) : m32;
+  block_max_to(__uint_as_float(bits), ts);
+}
+
+// amax after the Hadamard transform: 16 contiguous elements per lane, two
+// chunks per iteration
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_amax_rht(const void* __restrict__ x, int64_t nchunks,
+                                                       uint32_t rht_mask, float* __restrict__ ts) {
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; c + stride < nchunks; c += 2 * stride) {
+    float v[16], u[16];
+    load16<BF16>(x, c * 16, v);
+    load16<BF16>(x, (c + stride) * 16, u);
+    rht16(v, rht_mask);
+    rht16(u, rht_mask);
+    m = fmaxf(m, fmaxf(amax16(v), amax16(u)));
+  }
+  for (; c < nchunks; c += stride) {
+    float v[16];
+    load16<BF16>(x, c * 16, v);
+    rht16(v, rht_mask);
+    m = fmaxf(m, amax16(v));
+  }
+  block_max_to(m, ts);
 }
 
 // ------------------------------------------------------------ pass 2 -----
@@ -291,9 +345,15 @@ static int grid_stride_blocks(int64_t work, int cus) {
 
 template <bool BF16, bool RHT>
 static void launch_amax(const QuantArgs& a, int cus, hipStream_t st) {
-  const int64_t nchunks = a.rows * a.cols / 16;
-  hipLaunchKernelGGL((k_amax<BF16, RHT>), dim3(grid_stride_blocks(nchunks, cus)), dim3(kThreads), 0,
-                     st, a.x, nchunks, a.rht_mask, a.tensor_scale);
+  const int64_t n = a.rows * a.cols;
+  if (RHT) {
+    hipLaunchKernelGGL((k_amax_rht<BF16>), dim3(grid_stride_blocks(n / 16, cus)), dim3(kThreads), 0, st,
+                       a.x, n / 16, a.rht_mask, a.tensor_scale);
+  } else {
+    const int64_t nvec = n / (BF16 ? 8 : 4);  // 16-byte vectors (n % 16 == 0)
+    hipLaunchKernelGGL((k_amax_plain<BF16>), dim3(grid_stride_blocks(nvec / 4, cus)), dim3(kThreads), 0,
+                       st, reinterpret_cast<const uint4*>(a.x), nvec, a.tensor_scale);
+  }
 }
 
 template <bool BF16, bool RHT, bool SR>
