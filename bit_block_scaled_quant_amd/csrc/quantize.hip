@@ -63,7 +63,12 @@ __device__ __forceinline__ void block_max_to(float m, float* ts) {
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
-    atomicMax(reinterpret_cast<unsigned int*>(ts + 1), __float_as_uint(m));
+    // Same-address atomics serialize in L2: issue one only when this block's
+    // maximum beats the value already there (read past the L1; a stale
+    // value only costs an extra atomic).
+    unsigned int* t = reinterpret_cast<unsigned int*>(ts + 1);
+    const unsigned int bits = __float_as_uint(m);
+    if (bits > __hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(t, bits);
   }
 }
 
@@ -75,13 +80,14 @@ __global__ __launch_bounds__(kThreads) void k_amax_plain(const uint4* __restrict
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   for (; i + 3 * stride < nvec; i += 4 * stride) {
-    const uint4 a = x[i], b = x[i + stride], c = x[i + 2 * stride], d = x[i + 3 * stride];
+    const uint4 a = ld_stream(x + i), b = ld_stream(x + i + stride), c = ld_stream(x + i + 2 * stride),
+                d = ld_stream(x + i + 3 * stride);
     absmax_vec<BF16>(a, m16, m32);
     absmax_vec<BF16>(b, m16, m32);
     absmax_vec<BF16>(c, m16, m32);
     absmax_vec<BF16>(d, m16, m32);
   }
-  for (; i < nvec; i += stride) absmax_vec<BF16>(x[i], m16, m32);
+  for (; i < nvec; i += stride) absmax_vec<BF16>(ld_stream(x + i), m16, m32);
   const uint32_t bits = BF16 ? ((uint32_t)max(m16.x, m16.y) << 16) : m32;
   block_max_to(__uint_as_float(bits), ts);
 }
@@ -154,7 +160,7 @@ __device__ __forceinline__ void load16_stash(const void* __restrict__ x, int64_t
                                              typename TileElem<BF16>::T* trow, float v[16]) {
   if (BF16) {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e);
-    const uint4 a = p[0], b = p[1];
+    const uint4 a = ld_stream(p), b = ld_stream(p + 1);
     uint4* d = reinterpret_cast<uint4*>(trow);
     d[0] = a;
     d[1] = b;
@@ -165,16 +171,16 @@ __device__ __forceinline__ void load16_stash(const void* __restrict__ x, int64_t
       v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + e);
-    float4* d = reinterpret_cast<float4*>(trow);
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + e);
+    uint4* d = reinterpret_cast<uint4*>(trow);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float4 q = p[i];
+      const uint4 q = ld_stream(p + i);
       d[i] = q;
-      v[4 * i] = q.x;
-      v[4 * i + 1] = q.y;
-      v[4 * i + 2] = q.z;
-      v[4 * i + 3] = q.w;
+      v[4 * i] = __uint_as_float(q.x);
+      v[4 * i + 1] = __uint_as_float(q.y);
+      v[4 * i + 2] = __uint_as_float(q.z);
+      v[4 * i + 3] = __uint_as_float(q.w);
     }
   }
 }
@@ -338,20 +344,20 @@ __global__ __launch_bounds__(kThreads) void k_rht(const void* __restrict__ x, in
 }
 
 // ------------------------------------------------------------ launch -----
-static int grid_stride_blocks(int64_t work, int cus) {
+static int grid_stride_blocks(int64_t work, int cus, int per_cu = 8) {
   const int64_t want = (work + kThreads - 1) / kThreads;
-  return (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)cus * 8));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)cus * per_cu));
 }
 
 template <bool BF16, bool RHT>
 static void launch_amax(const QuantArgs& a, int cus, hipStream_t st) {
   const int64_t n = a.rows * a.cols;
   if (RHT) {
-    hipLaunchKernelGGL((k_amax_rht<BF16>), dim3(grid_stride_blocks(n / 16, cus)), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((k_amax_rht<BF16>), dim3(grid_stride_blocks(n / 16, cus, 4)), dim3(kThreads), 0, st,
                        a.x, n / 16, a.rht_mask, a.tensor_scale);
   } else {
     const int64_t nvec = n / (BF16 ? 8 : 4);  // 16-byte vectors (n % 16 == 0)
-    hipLaunchKernelGGL((k_amax_plain<BF16>), dim3(grid_stride_blocks(nvec / 4, cus)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((k_amax_plain<BF16>), dim3(grid_stride_blocks(nvec / 4, cus, 2)), dim3(kThreads), 0,
                        st, reinterpret_cast<const uint4*>(a.x), nvec, a.tensor_scale);
   }
 }
