@@ -423,6 +423,134 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_direct(GemmArgs g) {
   }
 }
 
+// ---- 8-wave variant of the fast path ------------------------------------
+// Same stages, layouts and unpack as k_gemm_direct, but 512 threads: eight
+// waves in a 2 x 4 grid, each owning 128 x 64 of the 256 x 256 tile, two per
+// SIMD.  A wave unpacks and multiplies in program order; the other wave on
+// the SIMD fills its VALU and LDS phases with matrix work.
+constexpr int kThreads8 = 512;
+
+__device__ __forceinline__ void dir8_issue(const GemmArgs& g, int64_t m0, int64_t n0, int64_t k0,
+                                           uint8_t* buf) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0..7
+  const int64_t kb = g.K / 2, ks = g.K / 16;
+  const uint8_t* a0 = g.a_codes + m0 * kb + k0 / 2;
+  const uint8_t* b0 = g.b_codes + n0 * kb + k0 / 2;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int blk = 4 * wave + u;  // 32 blocks of 1 KB per operand
+    const int row = 8 * blk + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    const uint32_t off = (uint32_t)(row * kb + 16 * chunk);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(a0 + off), (lds_void_t*)(buf + 1024 * blk), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(b0 + off), (lds_void_t*)(buf + kDirOffB + 1024 * blk),
+                                     16, 0, 0);
+  }
+  // scale planes: wave w fills plane w / 2, slots 128 * (w & 1) .. + 127
+  const int plane = wave >> 1;
+  const uint8_t* as0 = g.a_scales + m0 * ks + k0 / 16 + 4 * plane;
+  const uint8_t* bs0 = g.b_scales + n0 * ks + k0 / 16 + 4 * plane;
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int q = 128 * (wave & 1) + 64 * v + lane;
+    const int r = 128 * (q >> 7) + 16 * (q & 7) + ((q >> 3) & 15);
+    const uint32_t off = (uint32_t)(r * ks);
+    const int dst = 1024 * plane + 4 * (128 * (wave & 1) + 64 * v);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(as0 + off), (lds_void_t*)(buf + kDirOffAS + dst), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(bs0 + off), (lds_void_t*)(buf + kDirOffBS + dst), 4, 0, 0);
+  }
+}
+
+// one stage from buf for a 128 x 64 wave tile at rows wm*128, columns wn*64
+__device__ __forceinline__ void dir8_compute(const uint8_t* buf, floatx4 (&acc)[8][4], int wm, int wn,
+                                             int li, int lg) {
+  uint32_t da[8], db[4];
+  {
+    const uint4* pa = reinterpret_cast<const uint4*>(buf + kDirOffAS + 4 * (lg * 256 + wm * 128 + li * 8));
+    const uint4 x0 = pa[0], x1 = pa[1];
+    da[0] = x0.x; da[1] = x0.y; da[2] = x0.z; da[3] = x0.w;
+    da[4] = x1.x; da[5] = x1.y; da[6] = x1.z; da[7] = x1.w;
+    // B rows wn*64 + j*16 + li: half wn / 2, tile 4 * (wn & 1) + j of that half
+    const uint4 y = *reinterpret_cast<const uint4*>(buf + kDirOffBS +
+                                                    4 * (lg * 256 + (wn >> 1) * 128 + li * 8 + 4 * (wn & 1)));
+    db[0] = y.x; db[1] = y.y; db[2] = y.z; db[3] = y.w;
+  }
+#pragma unroll 1
+  for (int h = 0; h < 4; ++h) {
+    const int c = 2 * lg + (h >> 1), sub = 8 * (h & 1), sh = 8 * h;
+    uint2 qa[8], qb[4];
+    half2v sa[8], sb[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qa[i] = *reinterpret_cast<const uint2*>(buf + dswz(wm * 128 + i * 16 + li, c) + sub);
+      sa[i] = scale_h2(da[i] >> sh);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qb[j] = *reinterpret_cast<const uint2*>(buf + kDirOffB + dswz(wn * 64 + j * 16 + li, c) + sub);
+      sb[j] = scale_h2(db[j] >> sh);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      half8 fa[8], fb[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fa[i] = unpack8(s ? qa[i].y : qa[i].x, sa[i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = unpack8(s ? qb[j].y : qb[j].x, sb[j]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads8, 1) void k_gemm_direct8(GemmArgs g) {
+  __shared__ __align__(16) uint8_t buf0[kDirStage];
+  __shared__ __align__(16) uint8_t buf1[kDirStage];
+  const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * 256;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int li = lane & 15, lg = lane >> 4;
+
+  floatx4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t nk = g.K / kDirBK;  // even
+  dir8_issue(g, m0, n0, 0, buf0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; kt += 2) {
+    dir8_issue(g, m0, n0, (kt + 1) * kDirBK, buf1);
+    dir8_compute(buf0, acc, wm, wn, li, lg);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __syncthreads();
+    if (kt + 2 < nk) dir8_issue(g, m0, n0, (kt + 2) * kDirBK, buf0);
+    dir8_compute(buf1, acc, wm, wn, li, lg);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __syncthreads();
+  }
+
+  const float inv_a = __fdiv_rn(1.0f, g.a_ts[0]), inv_b = __fdiv_rn(1.0f, g.b_ts[0]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + wn * 64 + j * 16 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm * 128 + i * 16 + lg * 4 + r;
+        g.c[m * g.N + n] = (acc[i][j][r] * inv_a) * inv_b;
+      }
+    }
+  }
+}
+
 void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
   (void)cus;
   constexpr int BM = 256, BN = 256;
@@ -432,7 +560,7 @@ void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
                        ((uintptr_t)g.b_scales % 8 == 0);
   if (aligned && g.M % 256 == 0 && g.N % 256 == 0 && g.K % (2 * kDirBK) == 0 &&
       g.K <= (INT64_C(1) << 26) && (uintptr_t)g.a_scales % 4 == 0 && (uintptr_t)g.b_scales % 4 == 0)
-    hipLaunchKernelGGL(k_gemm_direct, grid, dim3(kGemmThreads), 0, st, g);
+    hipLaunchKernelGGL(k_gemm_direct8, grid, dim3(kThreads8), 0, st, g);
   else if (aligned)
     hipLaunchKernelGGL((k_gemm<BM, BN, true>), grid, dim3(kGemmThreads), 0, st, g);
   else
