@@ -12,18 +12,18 @@
 // so code * scale has at most 6 significant bits and lies in [2^-10, 2688]:
 // it is an exact, normal fp16 number.  Each operand element is rebuilt
 // exactly in fp16 in registers and multiplied on the fp16 MFMA
-// (v_mfma_f32_16x16x32_f16) with fp32 accumulation; the two tensor scales are
+// with fp32 accumulation; the two tensor scales are
 // applied once in the epilogue.  (gfx950's scaled FP4 MFMA takes power-of-two
 // scales per 32 elements, which cannot represent E4M3 scales per 16.)
 //
-// Tiling: a 256-thread workgroup owns a 256x256 tile of C and walks K in
-// steps of 128.  Packed codes and scale bytes are staged through LDS (double
-// buffered, 16-byte chunks XOR-swizzled against bank conflicts); each wave
-// owns a 128x128 sub-tile (accumulators in AGPRs), reads its packed
-// fragments from LDS and expands them in registers: per 128x128x32 of MFMA
-// work a lane converts 64 elements, which hides under the matrix cores.  Lane group g = lane / 16 of a fragment covers the 32
-// K-elements [32g, 32g+32) of a step; its word s feeds MFMA slice s.  A and B
-// use the same lane-to-K map, so the products pair up correctly.
+// Two kernels.  k_gemm (any shape): a 256-thread workgroup owns a 256x256
+// tile of C and walks K in steps of 128; packed codes and scale bytes are
+// staged through registers into LDS (double buffered, 16-byte chunks
+// XOR-swizzled against bank conflicts); each wave owns a 128x128 sub-tile,
+// reads its packed fragments from LDS and expands them in registers for
+// v_mfma_f32_16x16x32_f16.  Lane group g = lane / 16 of a fragment covers the
+// 32 K-elements [32g, 32g+32) of a step; its word s feeds MFMA slice s.
+// k_gemm_m32 (256-multiples, below) is the fast path.
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -261,19 +261,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   }
 }
 
-// ---- fast path: direct-to-LDS stages of 256 K-elements -----------------
+// ---- fast path: direct-to-LDS stages, 32 x 32 x 16 MFMA, pipelined unpack --
 // For M, N multiples of 256, K a multiple of 512 and aligned operands.
-// Same 256x256 tile, 128x128 per wave and exact unpack as k_gemm, but
-//  - a stage holds 256 K-elements (128 code bytes and 16 scale bytes per
-//    row), halving the barriers per K;
-//  - operand bytes go from global memory straight into LDS
+//  - A stage holds 256 K-elements of both operands (128 code bytes and 16
+//    scale bytes per row, 72 KB); two stages are double buffered in LDS.
+//  - Operand bytes go from global memory straight into LDS
 //    (global_load_lds_dwordx4 for codes, _dword for scales): no staging
-//    registers and no LDS store instructions;
-//  - in quarter h of a stage, lane group g of a fragment reads one whole
-//    NVFP4 block (K-elements 64g + 16h .. 64g + 16h + 15), so each lane needs
-//    one scale per tile and quarter; scales sit in LDS as four dword planes
-//    per operand, rows in (wave half, lane row, tile) order, and a lane reads
-//    the scales of all its tiles for the whole stage with two 16-byte reads.
+//    registers and no LDS store instructions.  Code rows are 8 XOR-swizzled
+//    16-byte chunks, so the 8 rows a wave reads at once hit distinct banks.
+//  - Four waves, one per SIMD, each own 128 x 128 of the 256 x 256 tile as
+//    4 x 4 tiles of v_mfma_f32_32x32x16_f16 (accumulators in AGPRs).
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
@@ -289,13 +286,25 @@ constexpr int kDirStage = kDirOffBS + kDirScales;  // 72 KB
 // physical 16-byte chunk of logical chunk c in row r (8 chunks per row)
 __device__ __forceinline__ int dswz(int r, int c) { return r * kDirRow + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
 
-// Direct loads of one stage (K-elements [k0, k0 + 256)) into buf.
-// Codes: 1 KB block blk = 8 * wave + u holds rows 8 * blk .. 8 * blk + 7;
-// lane l writes the 16-byte slot 64 * blk + l, i.e. row 8 * blk + l / 8 at
-// physical chunk l % 8, and fetches the logical chunk stored there.
-// Scales: dword slot 128 * wave + 64 * v + l (4 per wave... see below) holds
-// bytes 4p .. 4p + 3 (block columns 4p .. 4p + 3) of one row.
-__device__ __forceinline__ void dir_issue(const GemmArgs& g, int64_t m0, int64_t n0, int64_t k0,
+// Lane l feeds row l % 32 of a fragment; its lane group g = l / 32 covers the
+// NVFP4 blocks 8g .. 8g + 7 of a stage, so MFMA step t = 2p + s takes half s
+// of block 8g + p from each group (A and B use the same map, so the products
+// pair up).  A step's fragments take 32 VGPRs, which leaves room to unpack
+// step t + 1 while step t multiplies: the unpack and the LDS reads of the
+// next block are interleaved instruction by instruction with the 16 MFMAs of
+// a step (sched_group_barrier), so the vector ALU works under the matrix
+// core.  The barrier that publishes the next stage sits before a stage's
+// last step, whose MFMAs then cover the next stage's first reads and unpack.
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+struct M32Frag { half8 a[4], b[4]; };
+struct M32Raw { uint2 a[4], b[4]; };
+struct M32Scales { uint4 a[2], b[2]; };  // dword 2i + q: blocks 8g + 4q .. + 3 of tile-row i
+
+// Scale slots per operand (1024 dwords, 4 per stage row): slot
+// ((2g + w) * 32 + r) * 8 + 2i + q holds the four scale bytes of blocks
+// 8g + 4q .. 8g + 4q + 3 of row 128w + 32i + r.
+__device__ __forceinline__ void m32_issue(const GemmArgs& g, int64_t m0, int64_t n0, int64_t k0,
                                           uint8_t* buf) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -312,240 +321,179 @@ __device__ __forceinline__ void dir_issue(const GemmArgs& g, int64_t m0, int64_t
     __builtin_amdgcn_global_load_lds((glb_void_t*)(b0 + off), (lds_void_t*)(buf + kDirOffB + 1024 * blk),
                                      16, 0, 0);
   }
-  // 1024 dword slots per operand: slot = 256 * plane + q, q = 128 * half +
-  // 8 * li + i for row 128 * half + 16 * i + li; wave w covers slots
-  // 256 * w .. 256 * w + 255 (plane w) in four 64-slot pieces
-  const uint8_t* as0 = g.a_scales + m0 * ks + k0 / 16 + 4 * wave;
-  const uint8_t* bs0 = g.b_scales + n0 * ks + k0 / 16 + 4 * wave;
+  const uint8_t* as0 = g.a_scales + m0 * ks + k0 / 16;
+  const uint8_t* bs0 = g.b_scales + n0 * ks + k0 / 16;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int q = 64 * v + lane;
-    const int r = 128 * (q >> 7) + 16 * (q & 7) + ((q >> 3) & 15);
-    const uint32_t off = (uint32_t)(r * ks);
+    const int slot = 256 * v + 64 * wave + lane;
+    const int q = slot & 1, i = (slot >> 1) & 3, r = (slot >> 3) & 31, w = (slot >> 8) & 1, gg = slot >> 9;
+    const int row = 128 * w + 32 * i + r;
+    const uint32_t off = (uint32_t)(row * ks + 4 * (2 * gg + q));
     __builtin_amdgcn_global_load_lds((glb_void_t*)(as0 + off),
-                                     (lds_void_t*)(buf + kDirOffAS + 1024 * wave + 256 * v), 4, 0, 0);
+                                     (lds_void_t*)(buf + kDirOffAS + 1024 * v + 256 * wave), 4, 0, 0);
     __builtin_amdgcn_global_load_lds((glb_void_t*)(bs0 + off),
-                                     (lds_void_t*)(buf + kDirOffBS + 1024 * wave + 256 * v), 4, 0, 0);
+                                     (lds_void_t*)(buf + kDirOffBS + 1024 * v + 256 * wave), 4, 0, 0);
   }
 }
 
-// one stage of MFMA work from buf: four quarters, each one NVFP4 block per
-// lane group (two MFMA slices)
-__device__ __forceinline__ void dir_compute(const uint8_t* buf, floatx4 (&acc)[8][8], int wm, int wn,
-                                            int li, int lg) {
-  // scale dwords of plane lg (block columns 4g .. 4g + 3) for all tiles
-  uint32_t da[8], db[8];
-  {
-    const uint4* pa = reinterpret_cast<const uint4*>(buf + kDirOffAS + 4 * (lg * 256 + wm * 128 + li * 8));
-    const uint4* pb = reinterpret_cast<const uint4*>(buf + kDirOffBS + 4 * (lg * 256 + wn * 128 + li * 8));
-    const uint4 x0 = pa[0], x1 = pa[1], y0 = pb[0], y1 = pb[1];
-    da[0] = x0.x; da[1] = x0.y; da[2] = x0.z; da[3] = x0.w;
-    da[4] = x1.x; da[5] = x1.y; da[6] = x1.z; da[7] = x1.w;
-    db[0] = y0.x; db[1] = y0.y; db[2] = y0.z; db[3] = y0.w;
-    db[4] = y1.x; db[5] = y1.y; db[6] = y1.z; db[7] = y1.w;
+__device__ __forceinline__ void m32_read_scales(const uint8_t* buf, int wm, int wn, int r, int gq,
+                                                M32Scales& d) {
+  const uint4* pa = reinterpret_cast<const uint4*>(buf + kDirOffAS + 32 * ((2 * gq + wm) * 32 + r));
+  const uint4* pb = reinterpret_cast<const uint4*>(buf + kDirOffBS + 32 * ((2 * gq + wn) * 32 + r));
+  d.a[0] = pa[0]; d.a[1] = pa[1]; d.b[0] = pb[0]; d.b[1] = pb[1];
+}
+
+// raw codes of block 8g + p for the lane's four A and four B rows
+template <int P>
+__device__ __forceinline__ void m32_read_raw(const uint8_t* buf, int wm, int wn, int r, int gq, M32Raw& q) {
+  const int c = 4 * gq + (P >> 1), sub = 8 * (P & 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    q.a[i] = *reinterpret_cast<const uint2*>(buf + dswz(wm * 128 + i * 32 + r, c) + sub);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    q.b[j] = *reinterpret_cast<const uint2*>(buf + kDirOffB + dswz(wn * 128 + j * 32 + r, c) + sub);
+}
+
+__device__ __forceinline__ uint32_t m32_dword(const uint4& v0, const uint4& v1, int k) {
+  return k == 0 ? v0.x : k == 1 ? v0.y : k == 2 ? v0.z : k == 3 ? v0.w : k == 4 ? v1.x : k == 5 ? v1.y
+       : k == 6 ? v1.z : v1.w;
+}
+
+// step (P, S): half S of block 8g + P
+template <int P, int S>
+__device__ __forceinline__ void m32_unpack(const M32Raw& q, const M32Scales& d, M32Frag& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = unpack8(S ? q.a[i].y : q.a[i].x,
+                     scale_h2(m32_dword(d.a[0], d.a[1], 2 * i + (P >> 2)) >> (8 * (P & 3))));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    f.b[j] = unpack8(S ? q.b[j].y : q.b[j].x,
+                     scale_h2(m32_dword(d.b[0], d.b[1], 2 * j + (P >> 2)) >> (8 * (P & 3))));
+}
+
+__device__ __forceinline__ void m32_mfma(const M32Frag& f, floatx16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Instruction order of one step: 16 MFMAs; READS LDS reads ride on the
+// first MFMAs; with DEP the unpack waits on them behind a few MFMAs.
+template <int READS, bool DEP>
+__device__ __forceinline__ void m32_order() {
+#pragma unroll
+  for (int k = 0; k < READS; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, DEP ? 2 : 1, 0);
+    if (!DEP) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
   }
-#pragma unroll 1
-  for (int h = 0; h < 4; ++h) {
-    // block 4g + h: 8 bytes at logical chunk 2g + h / 2, byte 8 * (h & 1)
-    const int c = 2 * lg + (h >> 1), sub = 8 * (h & 1), sh = 8 * h;
-    uint2 qa[8], qb[8];
-    half2v sa[8], sb[8];
+  constexpr int kCover = DEP ? 3 : 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      qa[i] = *reinterpret_cast<const uint2*>(buf + dswz(wm * 128 + i * 16 + li, c) + sub);
-      sa[i] = scale_h2(da[i] >> sh);
-    }
+  for (int k = 0; k < kCover; ++k) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  constexpr int kRest = 16 - READS - kCover;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qb[j] = *reinterpret_cast<const uint2*>(buf + kDirOffB + dswz(wn * 128 + j * 16 + li, c) + sub);
-      sb[j] = scale_h2(db[j] >> sh);
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      half8 fa[8], fb[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) fa[i] = unpack8(s ? qa[i].y : qa[i].x, sa[i]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) fb[j] = unpack8(s ? qb[j].y : qb[j].x, sb[j]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
+  for (int k = 0; k < kRest; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, DEP ? 8 : 6, 0);
   }
 }
 
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_direct(GemmArgs g) {
+// pair P of a stage: steps 2P and 2P + 1.  In: f = step (P, 0), q = raw P.
+template <int P>
+__device__ __forceinline__ void m32_pair(const uint8_t* cur, M32Frag& f, M32Raw& q, const M32Scales& d,
+                                         floatx16 (&acc)[4][4], int wm, int wn, int r, int gq) {
+  M32Frag f1;
+  M32Raw qn;
+  m32_mfma(f, acc);
+  m32_read_raw<P + 1>(cur, wm, wn, r, gq, qn);
+  m32_unpack<P, 1>(q, d, f1);
+  m32_order<8, false>();
+  __builtin_amdgcn_sched_barrier(0);
+  m32_mfma(f1, acc);
+  m32_unpack<P + 1, 0>(qn, d, f);
+  m32_order<0, false>();
+  __builtin_amdgcn_sched_barrier(0);
+  q = qn;
+}
+
+// One stage from cur.  In: f = step (0, 0), q = raw 0, d = scales.  Out: the
+// same for the stage in nxt; after the barrier, when issue is set, stage
+// k_issue streams into cur (every wave is done reading it).
+__device__ __forceinline__ void m32_stage(const GemmArgs& g, int64_t m0, int64_t n0, bool issue,
+                                          int64_t k_issue, uint8_t* cur, const uint8_t* nxt, M32Frag& f,
+                                          M32Raw& q, M32Scales& d, floatx16 (&acc)[4][4], int wm, int wn,
+                                          int r, int gq) {
+  m32_pair<0>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<1>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<2>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<3>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<4>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<5>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<6>(cur, f, q, d, acc, wm, wn, r, gq);
+  M32Frag f1;
+  m32_mfma(f, acc);
+  m32_unpack<7, 1>(q, d, f1);
+  m32_order<0, false>();
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // waits for this wave's loads of nxt (vmcnt(0)), then all waves
+  if (issue) m32_issue(g, m0, n0, k_issue, cur);
+  __builtin_amdgcn_sched_barrier(0);
+  m32_mfma(f1, acc);
+  m32_read_scales(nxt, wm, wn, r, gq, d);
+  m32_read_raw<0>(nxt, wm, wn, r, gq, q);
+  m32_unpack<0, 0>(q, d, f);
+  m32_order<6, true>();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g) {
   __shared__ __align__(16) uint8_t buf0[kDirStage];
   __shared__ __align__(16) uint8_t buf1[kDirStage];
   const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * 256;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int li = lane & 15, lg = lane >> 4;
+  const int r = lane & 31, gq = lane >> 5;
 
-  floatx4 acc[8][8];
+  floatx16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const int64_t nk = g.K / kDirBK;  // even
-  dir_issue(g, m0, n0, 0, buf0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt(0) only
-  __syncthreads();
-  // Unrolled over the two buffers: a stage is computed from one buffer while
-  // the next stage streams into the other; the barrier after each stage
-  // publishes the streamed stage and frees the buffer just read.
-  for (int64_t kt = 0; kt < nk; kt += 2) {
-    dir_issue(g, m0, n0, (kt + 1) * kDirBK, buf1);
-    dir_compute(buf0, acc, wm, wn, li, lg);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __syncthreads();
-    if (kt + 2 < nk) dir_issue(g, m0, n0, (kt + 2) * kDirBK, buf0);
-    dir_compute(buf1, acc, wm, wn, li, lg);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __syncthreads();
-  }
-
-  const float inv_a = __fdiv_rn(1.0f, g.a_ts[0]), inv_b = __fdiv_rn(1.0f, g.b_ts[0]);
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t n = n0 + wn * 128 + j * 16 + li;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm * 128 + i * 16 + lg * 4 + r;
-        g.c[m * g.N + n] = (acc[i][j][r] * inv_a) * inv_b;
-      }
-    }
-  }
-}
-
-// ---- 8-wave variant of the fast path ------------------------------------
-// Same stages, layouts and unpack as k_gemm_direct, but 512 threads: eight
-// waves in a 2 x 4 grid, each owning 128 x 64 of the 256 x 256 tile, two per
-// SIMD.  A wave unpacks and multiplies in program order; the other wave on
-// the SIMD fills its VALU and LDS phases with matrix work.
-constexpr int kThreads8 = 512;
-
-__device__ __forceinline__ void dir8_issue(const GemmArgs& g, int64_t m0, int64_t n0, int64_t k0,
-                                           uint8_t* buf) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0..7
-  const int64_t kb = g.K / 2, ks = g.K / 16;
-  const uint8_t* a0 = g.a_codes + m0 * kb + k0 / 2;
-  const uint8_t* b0 = g.b_codes + n0 * kb + k0 / 2;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int blk = 4 * wave + u;  // 32 blocks of 1 KB per operand
-    const int row = 8 * blk + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
-    const uint32_t off = (uint32_t)(row * kb + 16 * chunk);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(a0 + off), (lds_void_t*)(buf + 1024 * blk), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(b0 + off), (lds_void_t*)(buf + kDirOffB + 1024 * blk),
-                                     16, 0, 0);
-  }
-  // scale planes: wave w fills plane w / 2, slots 128 * (w & 1) .. + 127
-  const int plane = wave >> 1;
-  const uint8_t* as0 = g.a_scales + m0 * ks + k0 / 16 + 4 * plane;
-  const uint8_t* bs0 = g.b_scales + n0 * ks + k0 / 16 + 4 * plane;
-#pragma unroll
-  for (int v = 0; v < 2; ++v) {
-    const int q = 128 * (wave & 1) + 64 * v + lane;
-    const int r = 128 * (q >> 7) + 16 * (q & 7) + ((q >> 3) & 15);
-    const uint32_t off = (uint32_t)(r * ks);
-    const int dst = 1024 * plane + 4 * (128 * (wave & 1) + 64 * v);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(as0 + off), (lds_void_t*)(buf + kDirOffAS + dst), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(bs0 + off), (lds_void_t*)(buf + kDirOffBS + dst), 4, 0, 0);
-  }
-}
-
-// one stage from buf for a 128 x 64 wave tile at rows wm*128, columns wn*64
-__device__ __forceinline__ void dir8_compute(const uint8_t* buf, floatx4 (&acc)[8][4], int wm, int wn,
-                                             int li, int lg) {
-  uint32_t da[8], db[4];
-  {
-    const uint4* pa = reinterpret_cast<const uint4*>(buf + kDirOffAS + 4 * (lg * 256 + wm * 128 + li * 8));
-    const uint4 x0 = pa[0], x1 = pa[1];
-    da[0] = x0.x; da[1] = x0.y; da[2] = x0.z; da[3] = x0.w;
-    da[4] = x1.x; da[5] = x1.y; da[6] = x1.z; da[7] = x1.w;
-    // B rows wn*64 + j*16 + li: half wn / 2, tile 4 * (wn & 1) + j of that half
-    const uint4 y = *reinterpret_cast<const uint4*>(buf + kDirOffBS +
-                                                    4 * (lg * 256 + (wn >> 1) * 128 + li * 8 + 4 * (wn & 1)));
-    db[0] = y.x; db[1] = y.y; db[2] = y.z; db[3] = y.w;
-  }
-#pragma unroll 1
-  for (int h = 0; h < 4; ++h) {
-    const int c = 2 * lg + (h >> 1), sub = 8 * (h & 1), sh = 8 * h;
-    uint2 qa[8], qb[4];
-    half2v sa[8], sb[4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      qa[i] = *reinterpret_cast<const uint2*>(buf + dswz(wm * 128 + i * 16 + li, c) + sub);
-      sa[i] = scale_h2(da[i] >> sh);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      qb[j] = *reinterpret_cast<const uint2*>(buf + kDirOffB + dswz(wn * 64 + j * 16 + li, c) + sub);
-      sb[j] = scale_h2(db[j] >> sh);
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      half8 fa[8], fb[4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) fa[i] = unpack8(s ? qa[i].y : qa[i].x, sa[i]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = unpack8(s ? qb[j].y : qb[j].x, sb[j]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-  }
-}
-
-__global__ __launch_bounds__(kThreads8, 1) void k_gemm_direct8(GemmArgs g) {
-  __shared__ __align__(16) uint8_t buf0[kDirStage];
-  __shared__ __align__(16) uint8_t buf1[kDirStage];
-  const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * 256;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int li = lane & 15, lg = lane >> 4;
-
-  floatx4 acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < 16; ++k) acc[i][j][k] = 0.f;
 
   const int64_t nk = g.K / kDirBK;  // even
-  dir8_issue(g, m0, n0, 0, buf0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);
+  m32_issue(g, m0, n0, 0, buf0);
   __syncthreads();
+  m32_issue(g, m0, n0, kDirBK, buf1);
+  M32Frag f;
+  M32Raw q;
+  M32Scales d;
+  m32_read_scales(buf0, wm, wn, r, gq, d);
+  m32_read_raw<0>(buf0, wm, wn, r, gq, q);
+  m32_unpack<0, 0>(q, d, f);
   for (int64_t kt = 0; kt < nk; kt += 2) {
-    dir8_issue(g, m0, n0, (kt + 1) * kDirBK, buf1);
-    dir8_compute(buf0, acc, wm, wn, li, lg);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __syncthreads();
-    if (kt + 2 < nk) dir8_issue(g, m0, n0, (kt + 2) * kDirBK, buf0);
-    dir8_compute(buf1, acc, wm, wn, li, lg);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __syncthreads();
+    m32_stage(g, m0, n0, kt + 2 < nk, (kt + 2) * kDirBK, buf0, buf1, f, q, d, acc, wm, wn, r, gq);
+    // on the last stage the reads of buf0 at its end are of stale data and unused
+    m32_stage(g, m0, n0, kt + 3 < nk, (kt + 3) * kDirBK, buf1, buf0, f, q, d, acc, wm, wn, r, gq);
   }
 
+  // D layout of the 32 x 32 MFMA: lane l, value k -> column l % 32, row
+  // 8 * (k / 4) + 4 * (l / 32) + k % 4
   const float inv_a = __fdiv_rn(1.0f, g.a_ts[0]), inv_b = __fdiv_rn(1.0f, g.b_ts[0]);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 16 + li;
+      const int64_t n = n0 + wn * 128 + j * 32 + r;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm * 128 + i * 16 + lg * 4 + r;
-        g.c[m * g.N + n] = (acc[i][j][r] * inv_a) * inv_b;
+      for (int k = 0; k < 16; ++k) {
+        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (k >> 2) + 4 * gq + (k & 3);
+        g.c[m * g.N + n] = (acc[i][j][k] * inv_a) * inv_b;
       }
     }
   }
@@ -560,7 +508,7 @@ void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
                        ((uintptr_t)g.b_scales % 8 == 0);
   if (aligned && g.M % 256 == 0 && g.N % 256 == 0 && g.K % (2 * kDirBK) == 0 &&
       g.K <= (INT64_C(1) << 26) && (uintptr_t)g.a_scales % 4 == 0 && (uintptr_t)g.b_scales % 4 == 0)
-    hipLaunchKernelGGL(k_gemm_direct8, grid, dim3(kThreads8), 0, st, g);
+    hipLaunchKernelGGL(k_gemm_m32, grid, dim3(kGemmThreads), 0, st, g);
   else if (aligned)
     hipLaunchKernelGGL((k_gemm<BM, BN, true>), grid, dim3(kGemmThreads), 0, st, g);
   else

@@ -36,7 +36,8 @@ def check_full(c_gpu, ref, refabs):
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (64, 64, 128), (200, 136, 272),
                                    (130, 250, 512), (1, 1, 16), (17, 300, 48), (129, 129, 1024),
                                    (384, 128, 4096), (256, 256, 512), (512, 768, 1024),
-                                   (768, 256, 3072)])
+                                   (768, 256, 3072), (256, 256, 64), (512, 256, 448),
+                                   (256, 512, 320)])
 def test_gemm_small(M, N, K):
     a = datagen.tiny(tag=datagen.TAG_A, rows=M, cols=K, seed=M)
     b = datagen.tiny(tag=datagen.TAG_B, rows=N, cols=K, seed=N)
