@@ -18,9 +18,10 @@
 //                   16 rows, written as rows of the transpose): a 128x128
 //                   tile is staged in LDS so that both copies leave in
 //                   coalesced 64-byte row segments;
-//   k_encode_tile2d 16x16 blocks (2B.3): one scale per tile, each element
-//                   encoded once and written both ways, so the transposed
-//                   copy is bit-identical to quantizing W^T.
+//   k_encode_2d     16x16 blocks (2B.3): one wave per 16 x 64 strip, one
+//                   scale per block, each element encoded once and written
+//                   both ways, so the transposed copy is bit-identical to
+//                   quantizing W^T.
 // k_rht writes the transform of 2B.2 alone (fp32 output).
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
@@ -244,87 +245,228 @@ __global__ __launch_bounds__(kThreads) void k_encode_tile1d(
                               codes_t, scales_t);
 }
 
+// 2D (16 x 16) blocks: one wave per strip of 16 rows x 64 columns (four
+// blocks side by side); a workgroup covers 128 x 256 (each wave eight strips
+// down its 64 columns), one workgroup per tile.  Each lane loads eight
+// consecutive elements of two rows (rows g and g + 8, eight lanes per row,
+// so loads are 128-byte row segments); a block's 256 elements sit in sixteen
+// lanes, whose amax is a cross-lane reduction, and each lane encodes its own
+// elements (rowwise codes; the scale byte is replicated on every row of the
+// block).  The transposed copy is those codes transposed: the strip's
+// codes go through 512 bytes of LDS and every lane transposes one 8 x 8
+// nibble tile, so SR codes use the rowwise draws (element r * C + c,
+// stream 0) in both copies and the copy is bit-identical to quantizing W^T.
+constexpr int kStripCols = 64;
+
+// r[i] holds nibbles (i, 0..7) of an 8 x 8 nibble matrix; afterwards r[j]
+// holds nibbles (0..7, j): 16-bit, 8-bit, then 4-bit block swaps
+__device__ __forceinline__ void nib_transpose8(uint32_t r[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = r[i], b = r[i + 4];
+    r[i] = (a & 0x0000FFFFu) | (b << 16);
+    r[i + 4] = (a >> 16) | (b & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int h = 0; h < 8; h += 4)
+#pragma unroll
+    for (int i = h; i < h + 2; ++i) {
+      const uint32_t a = r[i], b = r[i + 2];
+      r[i] = (a & 0x00FF00FFu) | ((b & 0x00FF00FFu) << 8);
+      r[i + 2] = ((a >> 8) & 0x00FF00FFu) | (b & 0xFF00FF00u);
+    }
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t a = r[i], b = r[i + 1];
+    r[i] = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
+    r[i + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  }
+}
+
+// raw storage of eight consecutive input elements (e % 8 == 0)
+template <bool BF16>
+struct Raw8 {
+  uint4 a, b;  // b unused for bf16
+};
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> load8_raw(const void* __restrict__ x, int64_t e) {
+  Raw8<BF16> r;
+  if (BF16) {
+    r.a = ld_stream(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e));
+    r.b = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + e);
+    r.a = ld_stream(p);
+    r.b = ld_stream(p + 1);
+  }
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float v[8]) {
+  if (BF16) {
+    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y); v[2] = __uint_as_float(r.a.z);
+    v[3] = __uint_as_float(r.a.w); v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+    v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+  }
+}
+
+// codes of eight elements (element index0 .. index0 + 7, index0 % 8 == 0)
+template <bool SR>
+__device__ __forceinline__ uint32_t encode8(const float v[8], float inv, uint64_t seed, uint32_t stream,
+                                            uint64_t index0) {
+  float y[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = v[j] * inv;
+  if (SR) return e2m1_sr8(y, sr_draws(seed, stream, index0 >> 3));
+  return e2m1_rne8(y);
+}
+
+// max over the sixteen lanes of a DPP row (quad swaps, then rotations by 4
+// and 8 within the row)
+__device__ __forceinline__ float row16_max(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x124, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, true)));
+  return m;
+}
+
 template <bool BF16, bool SR>
-__global__ __launch_bounds__(kThreads) void k_encode_tile2d(
+__global__ __launch_bounds__(kThreads) void k_encode_2d(
     const void* __restrict__ x, int64_t R, int64_t C, uint64_t seed, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t,
     float* __restrict__ ts) {
-  using E = TileElem<BF16>;
-  constexpr int pitch = kTile + E::kPad;
-  constexpr int cpitch = kTile + 4;
-  __shared__ __align__(16) typename E::T tile[kTile * pitch];
-  __shared__ uint8_t qt[kTile * cpitch];  // one code per byte, [row][col]
-
+  // per wave: one strip's codes [row][8-column chunk], the tile's transposed
+  // codes [column][row / 8] and one strip's row scale words
+  __shared__ uint32_t qs_all[kThreads / 64][16 * 8];
+  __shared__ uint32_t tq_all[kThreads / 64][64 * 16];
+  __shared__ uint32_t rs_all[kThreads / 64][16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t* qs = qs_all[wv];
+  uint32_t* tq = tq_all[wv];
+  uint8_t* rs = reinterpret_cast<uint8_t*>(rs_all[wv]);
   const float s_enc = tensor_scale_from_amax(ts[1]);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) ts[0] = s_enc;
-  const int64_t r0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;
-  const int rows_in = (int)(R - r0 < kTile ? R - r0 : kTile);
-  const int cols_in = (int)(C - c0 < kTile ? C - c0 : kTile);
-
-#pragma unroll 1
-  for (int q = threadIdx.x; q < kTile * (kTile / 16); q += kThreads) {
-    const int row = q >> 3, cb = q & 7;
-    if (row >= rows_in || cb * 16 >= cols_in) continue;
-    float v[16];
-    load16_stash<BF16>(x, (r0 + row) * C + c0 + cb * 16, tile + row * pitch + cb * 16, v);
-  }
-  __syncthreads();
-
-  // four threads per 16x16 block, four rows each
-  const int blk = threadIdx.x >> 2, quarter = threadIdx.x & 3;
-  const int bi = blk >> 3, bj = blk & 7;
-  const bool valid = bi * 16 < rows_in && bj * 16 < cols_in;
-  float v[4][16];
-  float m = 0.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) ts[0] = s_enc;
+  const int64_t tiles_c = (C + 4 * kStripCols - 1) / (4 * kStripCols);
+  const int64_t ntiles = ((R + 127) / 128) * tiles_c;
+  // Workgroups are dealt to the eight XCDs in turn; tile numbers are laid
+  // out so that each XCD takes a contiguous run of tiles in row-major order,
+  // and output lines shared by neighbouring tiles are completed in one L2.
+  const int64_t per_xcd = (ntiles + 7) / 8;
+  const int64_t tile = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (tile >= ntiles) return;
+  // load/encode role: block b = lane / 16 (the lane's DPP row), rows g and
+  // g + 8 of the strip, column half hf; one load instruction covers eight
+  // whole 128-byte row segments
+  const int b = lane >> 4, g = (lane >> 1) & 7, hf = lane & 1, c = 2 * b + hf;
+  // transposition role: block, row half, column half, column pair
+  const int rh = (lane >> 3) & 1, ch = (lane >> 2) & 1, jq = lane & 3;
+  // a workgroup tile is 128 rows x 256 columns; wave wv walks down its
+  // 64-column strip, so every line of rowwise and of transposed codes is
+  // completed by one workgroup
+  const int64_t c0 = (tile % tiles_c) * (4 * kStripCols) + wv * kStripCols;
+  const int64_t rt = (tile / tiles_c) * 128;
+  if (c0 >= C) return;
+  const int64_t col = c0 + 8 * c;
+  const bool act = col < C;  // C % 16 == 0: both halves of a block agree
+  const int nstrips = (int)min<int64_t>(8, (R - rt) / 16);
+  uint32_t st_lo = 0u, st_hi = 0u;  // transposed scale bytes of column c0 + lane
+  // All of the tile's loads go out first (bf16: 64 VGPRs of raw data), so a
+  // wave has eight strips of reads in flight; fp32 input keeps two.
+  constexpr int kAhead = BF16 ? 8 : 2;
+  Raw8<BF16> ra[kAhead], rb[kAhead];
+  const int64_t e0 = (rt + g) * C + col;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = bi * 16 + quarter * 4 + i;
+  for (int i = 0; i < kAhead; ++i)
+    if (act && i < nstrips) {
+      ra[i] = load8_raw<BF16>(x, e0 + 16 * i * C);
+      rb[i] = load8_raw<BF16>(x, e0 + (16 * i + 8) * C);
+    }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[i][j] = valid ? E::to_float(tile[row * pitch + bj * 16 + j]) : 0.0f;
-    m = fmaxf(m, amax16(v[i]));
-  }
-  m = fmaxf(m, __shfl_xor(m, 1));
-  m = fmaxf(m, __shfl_xor(m, 2));
-  if (valid) {
+  for (int i = 0; i < 8; ++i) {
+    if (i >= nstrips) break;
+    const int64_t r0 = rt + i * 16;
+    const int64_t ea = e0 + 16 * i * C, eb = ea + 8 * C;
+    float va[8], vb[8];
+    unpack8<BF16>(ra[i % kAhead], va);
+    unpack8<BF16>(rb[i % kAhead], vb);
+    if (kAhead < 8 && act && i + kAhead < nstrips) {
+      ra[i % kAhead] = load8_raw<BF16>(x, ea + 16 * kAhead * C);
+      rb[i % kAhead] = load8_raw<BF16>(x, eb + 16 * kAhead * C);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fmaxf(fabsf(va[j]), fabsf(vb[j])));
+    m = row16_max(m);
     float inv;
     const uint32_t byte = block_scale(m, s_enc, &inv);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = bi * 16 + quarter * 4 + i;
-      const int64_t e = (r0 + row) * C + c0 + bj * 16;
-      const uint2 q = encode16<SR>(v[i], inv, seed, 0u, (uint64_t)e);
-      *reinterpret_cast<uint2*>(codes + e / 2) = q;
-      scales[e / 16] = (uint8_t)byte;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        qt[row * cpitch + bj * 16 + j] = (uint8_t)((q.x >> (4 * j)) & 15u);
-        qt[row * cpitch + bj * 16 + 8 + j] = (uint8_t)((q.y >> (4 * j)) & 15u);
+    uint32_t qa = 0u, qb = 0u;
+    if (act) {
+      qa = encode8<SR>(va, inv, seed, 0u, (uint64_t)ea);
+      qb = encode8<SR>(vb, inv, seed, 0u, (uint64_t)eb);
+      *reinterpret_cast<uint32_t*>(codes + ea / 2) = qa;
+      *reinterpret_cast<uint32_t*>(codes + eb / 2) = qb;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // row scales: byte b of word r is block b's scale (every row of a block)
+    if (hf == 0) {
+      rs[g * 4 + b] = (uint8_t)byte;
+      rs[(g + 8) * 4 + b] = (uint8_t)byte;
+    }
+    if (codes_t) {
+      qs[g * 8 + c] = qa;
+      qs[(g + 8) * 8 + c] = qb;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (lane < 16) {
+      // the strip's row scales: four blocks per row, fewer at a ragged edge
+      const int64_t rw = (r0 + lane) * (C / 16) + c0 / 16;
+      const uint32_t wsc = rs_all[wv][lane];
+      if ((C & 63) == 0 && ((uintptr_t)scales & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(scales + rw) = wsc;  // 4-byte aligned
+      } else {
+        for (int k = 0; k < 4 && c0 + 16 * k < C; ++k) scales[rw + k] = (uint8_t)(wsc >> (8 * k));
       }
     }
     if (codes_t) {
+      uint32_t t[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int64_t c = c0 + bj * 16 + quarter * 4 + k;
-        scales_t[c * (R / 16) + (r0 / 16) + bi] = (uint8_t)byte;
-      }
+      for (int k = 0; k < 8; ++k) t[k] = qs[(rh * 8 + k) * 8 + 2 * b + ch];
+      nib_transpose8(t);
+      // columns 16 b + 8 ch + 2 jq and the next one of the strip; rows
+      // r0 + 8 rh .. + 7, i.e. word 2 i + rh of the column's 128 rows
+      const uint32_t w0 = jq == 0 ? t[0] : jq == 1 ? t[2] : jq == 2 ? t[4] : t[6];
+      const uint32_t w1 = jq == 0 ? t[1] : jq == 1 ? t[3] : jq == 2 ? t[5] : t[7];
+      const int cl = 16 * b + 8 * ch + 2 * jq;
+      tq[cl * 16 + 2 * i + rh] = w0;
+      tq[(cl + 1) * 16 + 2 * i + rh] = w1;
+      // lane l: column c0 + l, in this lane's block b = l / 16
+      if (i < 4) st_lo |= byte << (8 * i);
+      else st_hi |= byte << (8 * (i - 4));
     }
   }
-  if (!codes_t) return;
-  __syncthreads();
-  // transposed codes: thread -> (column, 64-row half), 16 rows per 8 bytes
-  const int col = threadIdx.x >> 1, half = threadIdx.x & 1;
-  if (col >= cols_in) return;
-  const int64_t c = c0 + col;
-#pragma unroll 1
-  for (int rb = half * 4; rb < half * 4 + 4; ++rb) {
-    if (rb * 16 >= rows_in) break;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      lo |= (uint32_t)qt[(rb * 16 + j) * cpitch + col] << (4 * j);
-      hi |= (uint32_t)qt[(rb * 16 + 8 + j) * cpitch + col] << (4 * j);
-    }
-    *reinterpret_cast<uint2*>(codes_t + c * (R / 2) + (r0 + rb * 16) / 2) = make_uint2(lo, hi);
+  if (!codes_t || c0 + lane >= C) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  // column c0 + lane of the transposed copy: 8 bytes of codes per strip, the
+  // whole 64-byte line for a full tile
+  uint8_t* dct = codes_t + (c0 + lane) * (R / 2) + rt / 2;
+  const uint32_t* src = tq + lane * 16;
+  for (int i = 0; i < nstrips; ++i)
+    *reinterpret_cast<uint2*>(dct + 8 * i) = make_uint2(src[2 * i], src[2 * i + 1]);
+  uint8_t* dst = scales_t + (c0 + lane) * (R / 16) + rt / 16;
+  if (nstrips == 8 && (R / 16) % 8 == 0 && ((uintptr_t)scales_t & 7) == 0) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(st_lo, st_hi);
+  } else {
+    for (int i = 0; i < nstrips; ++i) dst[i] = (uint8_t)((i < 4 ? st_lo >> (8 * i) : st_hi >> (8 * (i - 4))));
   }
 }
 
@@ -371,14 +513,17 @@ static void launch_rows(const QuantArgs& a, int cus, hipStream_t st) {
 }
 
 template <bool BF16, bool SR>
-static void launch_tile(const QuantArgs& a, bool two_d, hipStream_t st) {
-  const dim3 grid((unsigned)((a.cols + kTile - 1) / kTile), (unsigned)((a.rows + kTile - 1) / kTile));
-  if (two_d)
-    hipLaunchKernelGGL((k_encode_tile2d<BF16, SR>), grid, dim3(kThreads), 0, st, a.x, a.rows, a.cols,
+static void launch_tile(const QuantArgs& a, bool two_d, int cus, hipStream_t st) {
+  if (two_d) {
+    const int64_t tiles = ((a.rows + 127) / 128) * ((a.cols + 4 * kStripCols - 1) / (4 * kStripCols));
+    const int blocks = (int)(((tiles + 7) / 8) * 8);  // tiles <= 2^25 (rows * cols <= 2^40)
+    hipLaunchKernelGGL((k_encode_2d<BF16, SR>), dim3(blocks), dim3(kThreads), 0, st, a.x, a.rows, a.cols,
                        a.seed, a.codes, a.scales, a.codes_t, a.scales_t, a.tensor_scale);
-  else
+  } else {
+    const dim3 grid((unsigned)((a.cols + kTile - 1) / kTile), (unsigned)((a.rows + kTile - 1) / kTile));
     hipLaunchKernelGGL((k_encode_tile1d<BF16, SR>), grid, dim3(kThreads), 0, st, a.x, a.rows, a.cols,
                        a.seed, a.codes, a.scales, a.codes_t, a.scales_t, a.tensor_scale);
+  }
 }
 
 template <bool BF16>
@@ -391,9 +536,9 @@ static void launch_quantize_t(const QuantArgs& a, int cus, hipStream_t st) {
   const bool sr = a.rounding == 1;
   if (a.two_d || a.codes_t) {
     if (sr)
-      launch_tile<BF16, true>(a, a.two_d, st);
+      launch_tile<BF16, true>(a, a.two_d, cus, st);
     else
-      launch_tile<BF16, false>(a, a.two_d, st);
+      launch_tile<BF16, false>(a, a.two_d, cus, st);
   } else if (a.rht) {
     if (sr)
       launch_rows<BF16, true, true>(a, cus, st);
