@@ -34,23 +34,24 @@ constexpr float kFltMax = 3.40282346638528859812e+38f;
 
 // ---------------------------------------------------------------- E4M3 ---
 // s >= 0, finite or +inf.  Round to nearest even, saturate to 448 (0x7E).
+// Both ranges are computed and selected, so a wavefront does not diverge.
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  if (!(s < 448.0f)) return 0x7Eu;
   const uint32_t b = __float_as_uint(s);
-  if (b < 0x3C800000u) {  // s < 2^-6: subnormal range, multiples of 2^-9
-    // s * 512 is exact; rintf rounds half to even; 8 is the smallest normal
-    return (uint32_t)__builtin_rintf(s * 512.0f);
-  }
-  // keep 3 mantissa bits, round to nearest even on the discarded 20 bits
+  // s < 2^-6: subnormal range, multiples of 2^-9; s * 512 is exact and
+  // rintf rounds half to even (8 is the smallest normal)
+  const uint32_t sub = (uint32_t)__builtin_rintf(s * 512.0f);
+  // otherwise keep 3 mantissa bits, round to nearest even on the discarded 20
   const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
-  const uint32_t e = (r >> 23) - 120u;  // E4M3 exponent field (bias 7)
-  return (e << 3) | ((r >> 20) & 7u);
+  const uint32_t nrm = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);  // exponent bias 7
+  const uint32_t v = b < 0x3C800000u ? sub : nrm;
+  return s < 448.0f ? v : 0x7Eu;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t byte) {
   const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
-  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9, exact
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float sub = (float)m * 0.001953125f;  // m * 2^-9, exact
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e == 0 ? sub : nrm;
 }
 
 // ---------------------------------------------------------- scales -------
@@ -66,7 +67,8 @@ __device__ __forceinline__ uint32_t block_scale(float amax_b, float s_enc, float
   const float s = __fdiv_rn(t, 6.0f);
   const uint32_t byte = e4m3_encode(s);
   const float sb = e4m3_decode(byte);
-  *inv = (sb == 0.0f) ? 0.0f : fminf(__fdiv_rn(s_enc, sb), kFltMax);
+  const float q = fminf(__fdiv_rn(s_enc, sb), kFltMax);  // +inf for sb == 0, not used then
+  *inv = (sb == 0.0f) ? 0.0f : q;
   return byte;
 }
 
@@ -74,6 +76,15 @@ __device__ __forceinline__ uint32_t block_scale(float amax_b, float s_enc, float
 struct Philox4 {
   uint32_t x, y, z, w;
 };
+
+// a ^ b ^ c; one v_bitop3_b32 on the device
+__host__ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+#else
+  return a ^ b ^ c;
+#endif
+}
 
 // Ten rounds; in each, words 0 and 2 are multiplied by the round constants,
 // the high halves are xored with words 1 and 3 and the key, and the key is
@@ -85,7 +96,7 @@ __host__ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t 
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0), n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
     c0 = n0;
     c1 = (uint32_t)p1;
     c2 = n2;
