@@ -70,7 +70,7 @@ def test_quantize_columnwise(shape, dtype, rounding):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("rounding", [0, 1])
-@pytest.mark.parametrize("shape", SMALL + [(400, 48)])
+@pytest.mark.parametrize("shape", SMALL + [(400, 48), (384, 512)])
 def test_quantize_2d(shape, dtype, rounding):
     w = datagen.weight(out_features=shape[0], in_features=shape[1], seed=shape[0] + shape[1])
     w = w.float() if dtype == "f32" else w
