@@ -145,6 +145,43 @@ __device__ __forceinline__ void rht16(float v[16], uint32_t mask) {
   for (int j = 0; j < 16; ++j) v[j] = 0.25f * v[j];
 }
 
+// The same transform on a block held by a lane pair: the even lane holds
+// elements 0..7, the odd lane 8..15.  Stages h = 1, 2, 4 stay inside the
+// lane; stage h = 8 pairs element j of the two lanes through a DPP swap of
+// lanes 2k and 2k + 1 (all lanes of the wave must be active).  Every value
+// takes the same operations in the same order as rht16.
+__device__ __forceinline__ float lane_pair_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
+template <bool QUARTER = true>
+__device__ __forceinline__ void rht16_pair(float v[8], uint32_t mask, bool odd) {
+  const uint32_t m8 = odd ? (mask >> 8) : mask;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((m8 >> j) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+  // h = 8: even lane a + b (a its own), odd lane a - b (b its own)
+  const uint32_t neg = odd ? 0x80000000u : 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = lane_pair_swap(v[j]);
+    v[j] = p + __uint_as_float(__float_as_uint(v[j]) ^ neg);
+  }
+  if (QUARTER) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.25f * v[j];
+  }
+}
+
 // ----------------------------------------------------------- loads -------
 // Streaming 16-byte load with the nontemporal hint: the quantizer reads
 // every input byte once per pass, and on MI355X such loads sustain about
@@ -204,20 +241,21 @@ __device__ __forceinline__ uint32_t e2m1_rne8(const float* y) {
 // Stochastic rounding of eight values (the eight draws of one Philox call)
 // with the gfx950 conversion v_cvt_scalef32_sr_pk_fp4_f32, one value per
 // instruction (the second input is 0.0, whose code is 0).  Measured on the
-// device: the instruction rounds |v| up iff its discarded bits, read as a
-// fraction of the E2M1 step, plus rand[31:10] / 2^22 reach 1.  With
-// rand = ~(u << 16) that is exactly "u < f * 2^16" whenever the step
-// leaves 22 discarded bits (|v| >= 1); below that the hardware ignores the
-// discarded bits past the 22nd, so |v| is first rounded up to a multiple of
-// 2^-23 (exact, sign kept), which moves every fraction f*2^16 in (u, u+2^-6)
-// to a value the 22-bit comparison orders the same way.  An exhaustive
-// device test checks the result against the oracle's rule for every fp32
-// value in [2^-9, 6] and a sample of smaller ones.
+// device: the instruction divides its input by the scale operand and rounds
+// |v| up iff its discarded bits, read as a fraction of the E2M1 step, plus
+// rand[31:10] / 2^22 reach 1.  With rand = ~(u << 16) that is exactly
+// "u < f * 2^16" whenever the step leaves 22 discarded bits (|v| >= 1);
+// below that the hardware ignores the discarded bits past the 22nd, so |v|
+// is first rounded up to a multiple of 2^-23 (exact, sign kept), which moves
+// every fraction f*2^16 in (u, u+2^-6) to a value the 22-bit comparison
+// orders the same way.  The rounded value is passed as the integer
+// ceil(|v| 2^23) (with v's sign) and scale 2^23.  An exhaustive device test
+// checks the result against the oracle's rule for every fp32 value in
+// [2^-9, 6] and a sample of smaller ones.
 typedef float float2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float sr_prepare(float v) {
-  const float a = __builtin_ceilf(__builtin_fabsf(v) * 8388608.0f) * 1.1920928955078125e-7f;
-  return __builtin_copysignf(a, v);
+  return __builtin_copysignf(__builtin_ceilf(__builtin_fabsf(v) * 8388608.0f), v);
 }
 
 // One conversion into byte K of w; the other bytes of w are kept.  Written
@@ -228,13 +266,15 @@ __device__ __forceinline__ float sr_prepare(float v) {
 template <int K>
 __device__ __forceinline__ void sr_cvt(uint32_t& w, float v, uint32_t rand) {
   const float2v src = {sr_prepare(v), 0.0f};
-  if (K == 0) asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(w) : "v"(src), "v"(rand));
+  const float sc = 8388608.0f;  // 2^23
+  if (K == 0)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "+v"(w) : "v"(src), "v"(rand), "s"(sc));
   if (K == 1)
-    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(w) : "v"(src), "v"(rand));
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]" : "+v"(w) : "v"(src), "v"(rand), "s"(sc));
   if (K == 2)
-    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(w) : "v"(src), "v"(rand));
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]" : "+v"(w) : "v"(src), "v"(rand), "s"(sc));
   if (K == 3)
-    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(w) : "v"(src), "v"(rand));
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,1]" : "+v"(w) : "v"(src), "v"(rand), "s"(sc));
 }
 
 // elements 2K (draw: low half of word K) and 2K + 1 (high half) into byte K

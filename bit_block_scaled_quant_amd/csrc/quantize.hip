@@ -31,6 +31,53 @@ namespace nvfp4 {
 constexpr int kThreads = 256;
 constexpr int kTile = 128;
 
+// raw storage of eight consecutive input elements (e % 8 == 0)
+template <bool BF16>
+struct Raw8 {
+  uint4 a, b;  // b unused for bf16
+};
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> load8_raw(const void* __restrict__ x, int64_t e) {
+  Raw8<BF16> r;
+  if (BF16) {
+    r.a = ld_stream(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e));
+    r.b = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + e);
+    r.a = ld_stream(p);
+    r.b = ld_stream(p + 1);
+  }
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float v[8]) {
+  if (BF16) {
+    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y); v[2] = __uint_as_float(r.a.z);
+    v[3] = __uint_as_float(r.a.w); v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+    v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+  }
+}
+
+// codes of eight elements (element index0 .. index0 + 7, index0 % 8 == 0)
+template <bool SR>
+__device__ __forceinline__ uint32_t encode8(const float v[8], float inv, uint64_t seed, uint32_t stream,
+                                            uint64_t index0) {
+  float y[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = v[j] * inv;
+  if (SR) return e2m1_sr8(y, sr_draws(seed, stream, index0 >> 3));
+  return e2m1_rne8(y);
+}
+
 // ------------------------------------------------------------ pass 1 -----
 __global__ void k_init_amax(float* ts) {
   ts[0] = 0.0f;
@@ -93,34 +140,108 @@ __global__ __launch_bounds__(kThreads) void k_amax_plain(const uint4* __restrict
   block_max_to(__uint_as_float(bits), ts);
 }
 
-// amax after the Hadamard transform: 16 contiguous elements per lane, two
-// chunks per iteration
+// amax after the Hadamard transform.  A wave takes 1024 elements (64
+// blocks) at a time as two 512-element halves: lane l holds elements
+// 8l .. 8l + 7 of each, so every load instruction reads 1 KB of whole lines,
+// and a block sits in lanes 2k, 2k + 1 (rht16_pair).  Two such pieces per
+// iteration keep four loads in flight per lane.
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_amax_rht(const void* __restrict__ x, int64_t nchunks,
+__global__ __launch_bounds__(kThreads) void k_amax_rht(const void* __restrict__ x, int64_t nblk,
                                                        uint32_t rht_mask, float* __restrict__ ts) {
+  const int lane = threadIdx.x & 63;
+  const bool odd = lane & 1;
+  const int64_t npiece = (nblk + 31) / 32;  // 512 elements per piece
+  const int64_t wstride = (int64_t)gridDim.x * (kThreads / 64);
   float m = 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; c + stride < nchunks; c += 2 * stride) {
-    float v[16], u[16];
-    load16<BF16>(x, c * 16, v);
-    load16<BF16>(x, (c + stride) * 16, u);
-    rht16(v, rht_mask);
-    rht16(u, rht_mask);
-    m = fmaxf(m, fmaxf(amax16(v), amax16(u)));
+  for (int64_t pc = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 2; pc < npiece;
+       pc += 2 * wstride) {
+    Raw8<BF16> r[2];
+    bool valid[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t blk = (pc + u) * 32 + (lane >> 1);
+      valid[u] = pc + u < npiece && blk < nblk;
+      if (valid[u]) r[u] = load8_raw<BF16>(x, blk * 16 + 8 * odd);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float v[8];
+      if (valid[u]) {
+        unpack8<BF16>(r[u], v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+      }
+      rht16_pair<false>(v, rht_mask, odd);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    }
   }
-  for (; c < nchunks; c += stride) {
-    float v[16];
-    load16<BF16>(x, c * 16, v);
-    rht16(v, rht_mask);
-    m = fmaxf(m, amax16(v));
-  }
-  block_max_to(m, ts);
+  // the transform's final 1/4, applied to the maximum: rounding is monotone,
+  // so max |fl(v / 4)| = fl(max |v| / 4)
+  block_max_to(0.25f * m, ts);
 }
 
 // ------------------------------------------------------------ pass 2 -----
+// 1x16 blocks along rows (RNE).  A wave takes 1024 elements (64 blocks) at a time
+// as two halves: lane l holds elements 8l .. 8l + 7 of each, so loads read
+// 1 KB of whole lines per instruction and code stores write 256 contiguous
+// bytes; a block sits in lanes 2k, 2k + 1, whose amax is one DPP swap.
 template <bool BF16, bool RHT, bool SR>
 __global__ __launch_bounds__(kThreads) void k_encode_rows(const void* __restrict__ x, int64_t nblk,
+                                                          uint64_t seed, uint32_t rht_mask,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales,
+                                                          float* __restrict__ ts) {
+  const float s_enc = tensor_scale_from_amax(ts[1]);
+  if (blockIdx.x == 0 && threadIdx.x == 0) ts[0] = s_enc;
+  const int lane = threadIdx.x & 63;
+  const bool odd = lane & 1;
+  const int64_t npiece = (nblk + 31) / 32;  // 512 elements per piece
+  const int64_t wstride = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t pc = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 2; pc < npiece;
+       pc += 2 * wstride) {
+    Raw8<BF16> r[2];
+    bool valid[2];
+    int64_t blk[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      blk[u] = (pc + u) * 32 + (lane >> 1);
+      valid[u] = pc + u < npiece && blk[u] < nblk;  // a lane pair agrees
+      if (valid[u]) r[u] = load8_raw<BF16>(x, blk[u] * 16 + 8 * odd);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float v[8];
+      if (valid[u]) {
+        unpack8<BF16>(r[u], v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+      }
+      if (RHT) rht16_pair(v, rht_mask, odd);
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+      m = fmaxf(m, lane_pair_swap(m));
+      float inv;
+      const uint32_t byte = block_scale(m, s_enc, &inv);
+      if (valid[u]) {
+        // rowwise: block b covers elements 16b .. 16b + 15 of the row-major tensor
+        const int64_t e = blk[u] * 16 + 8 * odd;
+        *reinterpret_cast<uint32_t*>(codes + e / 2) = encode8<SR>(v, inv, seed, 0u, (uint64_t)e);
+        if (!odd) scales[blk[u]] = (uint8_t)byte;
+      }
+    }
+  }
+}
+
+// One thread per 16-element block, two 16-byte loads each: the layout for
+// SR and for the Hadamard transform, whose encodes are bound by vector ALU
+// work (Philox, the conversions, the butterfly), so that each block's scale
+// and transform are computed by one lane rather than two.
+template <bool BF16, bool RHT, bool SR>
+__global__ __launch_bounds__(kThreads) void k_encode_rows_blk(const void* __restrict__ x, int64_t nblk,
                                                           uint64_t seed, uint32_t rht_mask,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales,
@@ -281,53 +402,6 @@ __device__ __forceinline__ void nib_transpose8(uint32_t r[8]) {
     r[i] = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
     r[i + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
   }
-}
-
-// raw storage of eight consecutive input elements (e % 8 == 0)
-template <bool BF16>
-struct Raw8 {
-  uint4 a, b;  // b unused for bf16
-};
-
-template <bool BF16>
-__device__ __forceinline__ Raw8<BF16> load8_raw(const void* __restrict__ x, int64_t e) {
-  Raw8<BF16> r;
-  if (BF16) {
-    r.a = ld_stream(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e));
-    r.b = make_uint4(0u, 0u, 0u, 0u);
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + e);
-    r.a = ld_stream(p);
-    r.b = ld_stream(p + 1);
-  }
-  return r;
-}
-
-template <bool BF16>
-__device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float v[8]) {
-  if (BF16) {
-    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-    v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y); v[2] = __uint_as_float(r.a.z);
-    v[3] = __uint_as_float(r.a.w); v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
-    v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
-  }
-}
-
-// codes of eight elements (element index0 .. index0 + 7, index0 % 8 == 0)
-template <bool SR>
-__device__ __forceinline__ uint32_t encode8(const float v[8], float inv, uint64_t seed, uint32_t stream,
-                                            uint64_t index0) {
-  float y[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) y[j] = v[j] * inv;
-  if (SR) return e2m1_sr8(y, sr_draws(seed, stream, index0 >> 3));
-  return e2m1_rne8(y);
 }
 
 // max over the sixteen lanes of a DPP row (quad swaps, then rotations by 4
@@ -539,7 +613,7 @@ static void launch_amax(const QuantArgs& a, int cus, hipStream_t st) {
   const int64_t n = a.rows * a.cols;
   if (RHT) {
     hipLaunchKernelGGL((k_amax_rht<BF16>), dim3(grid_stride_blocks(n / 16, cus, 4)), dim3(kThreads), 0, st,
-                       a.x, n / 16, a.rht_mask, a.tensor_scale);
+                       a.x, n / 16, a.rht_mask, a.tensor_scale);  // n / 16 blocks
   } else {
     const int64_t nvec = n / (BF16 ? 8 : 4);  // 16-byte vectors (n % 16 == 0)
     hipLaunchKernelGGL((k_amax_plain<BF16>), dim3(grid_stride_blocks(nvec / 4, cus, 2)), dim3(kThreads), 0,
@@ -550,9 +624,14 @@ static void launch_amax(const QuantArgs& a, int cus, hipStream_t st) {
 template <bool BF16, bool RHT, bool SR>
 static void launch_rows(const QuantArgs& a, int cus, hipStream_t st) {
   const int64_t nblk = a.rows * a.cols / 16;
-  hipLaunchKernelGGL((k_encode_rows<BF16, RHT, SR>), dim3(grid_stride_blocks(nblk, cus)),
-                     dim3(kThreads), 0, st, a.x, nblk, a.seed, a.rht_mask, a.codes, a.scales,
-                     a.tensor_scale);
+  if (SR || RHT)
+    hipLaunchKernelGGL((k_encode_rows_blk<BF16, RHT, SR>), dim3(grid_stride_blocks(nblk, cus)),
+                       dim3(kThreads), 0, st, a.x, nblk, a.seed, a.rht_mask, a.codes, a.scales,
+                       a.tensor_scale);
+  else
+    hipLaunchKernelGGL((k_encode_rows<BF16, RHT, SR>), dim3(grid_stride_blocks(nblk, cus)),
+                       dim3(kThreads), 0, st, a.x, nblk, a.seed, a.rht_mask, a.codes, a.scales,
+                       a.tensor_scale);
 }
 
 template <bool BF16, bool SR>
