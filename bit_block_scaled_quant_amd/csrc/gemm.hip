@@ -276,12 +276,6 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 
 constexpr int kDirBK = 256;                     // K-elements per stage
 constexpr int kDirRow = kDirBK / 2;             // 128 code bytes per row
-constexpr int kDirCodes = 256 * kDirRow;        // 32 KB per operand
-constexpr int kDirScales = 256 * (kDirBK / 16);  // 4 KB per operand
-constexpr int kDirOffB = kDirCodes;
-constexpr int kDirOffAS = 2 * kDirCodes;
-constexpr int kDirOffBS = kDirOffAS + kDirScales;
-constexpr int kDirStage = kDirOffBS + kDirScales;  // 72 KB
 
 // physical 16-byte chunk of logical chunk c in row r (8 chunks per row)
 __device__ __forceinline__ int dswz(int r, int c) { return r * kDirRow + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
@@ -297,20 +291,55 @@ __device__ __forceinline__ int dswz(int r, int c) { return r * kDirRow + ((c ^ (
 // last step, whose MFMAs then cover the next stage's first reads and unpack.
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-struct M32Frag { half8 a[4], b[4]; };
-struct M32Raw { uint2 a[4], b[4]; };
-struct M32Scales { uint4 a[2], b[2]; };  // dword 2i + q: blocks 8g + 4q .. + 3 of tile-row i
+// NT = 32-column MFMA tiles per wave along N: 4 for a 256 x 256 workgroup
+// tile, 2 for 256 x 128 (used for the last, partial wave of tiles).
+template <int NT>
+struct M32 {
+  static constexpr int kBN = 64 * NT;                 // tile width
+  static constexpr int kLogNT = NT == 4 ? 2 : 1;
+  static constexpr int kOffB = 256 * kDirRow;         // B codes after 32 KB of A codes
+  static constexpr int kOffAS = kOffB + kBN * kDirRow;  // A scales, 4 KB
+  static constexpr int kOffBS = kOffAS + 4096;          // B scales, NT KB
+  static constexpr int kStage = kOffBS + 1024 * NT;
+};
 
-// Scale slots per operand (1024 dwords, 4 per stage row): slot
-// ((2g + w) * 32 + r) * 8 + 2i + q holds the four scale bytes of blocks
-// 8g + 4q .. 8g + 4q + 3 of row 128w + 32i + r.
+template <int NT>
+struct M32Frag { half8 a[4], b[NT]; };
+template <int NT>
+struct M32Raw { uint2 a[4], b[NT]; };
+template <int NT>
+struct M32Scales { uint4 a[2], b[(NT + 1) / 2]; };  // dword 2i + q: blocks 8g + 4q .. + 3 of tile-row i
+
+// Scale slots of an operand with 2 x NT tile-rows per wave half (A: NT = 4):
+// slot ((2g + w) * 32 + r) * 2NT + 2i + q holds the four scale bytes of blocks
+// 8g + 4q .. 8g + 4q + 3 of row (rows / 2) w + 32 i + r.
+template <int NT>
+__device__ __forceinline__ void m32_issue_scales(const uint8_t* s0, int64_t ks, uint8_t* dst) {
+  constexpr int kLog = NT == 4 ? 2 : 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int v = 0; v < NT; ++v) {
+    const int slot = 256 * v + 64 * wave + lane;
+    const int q = slot & 1, i = (slot >> 1) & (NT - 1), r = (slot >> (1 + kLog)) & 31;
+    const int w = (slot >> (6 + kLog)) & 1, gg = slot >> (7 + kLog);
+    const int row = 32 * NT * w + 32 * i + r;
+    const uint32_t off = (uint32_t)(row * ks + 4 * (2 * gg + q));
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(s0 + off), (lds_void_t*)(dst + 1024 * v + 256 * wave), 4,
+                                     0, 0);
+  }
+}
+
+template <int NT>
 __device__ __forceinline__ void m32_issue(const GemmArgs& g, int64_t m0, int64_t n0, int64_t k0,
                                           uint8_t* buf) {
+  using L = M32<NT>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t kb = g.K / 2, ks = g.K / 16;
   const uint8_t* a0 = g.a_codes + m0 * kb + k0 / 2;
   const uint8_t* b0 = g.b_codes + n0 * kb + k0 / 2;
+  // 1 KB blocks of 8 rows: 32 for A, 8 NT for B
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int blk = 8 * wave + u;
@@ -318,41 +347,41 @@ __device__ __forceinline__ void m32_issue(const GemmArgs& g, int64_t m0, int64_t
     const int chunk = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
     const uint32_t off = (uint32_t)(row * kb + 16 * chunk);
     __builtin_amdgcn_global_load_lds((glb_void_t*)(a0 + off), (lds_void_t*)(buf + 1024 * blk), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(b0 + off), (lds_void_t*)(buf + kDirOffB + 1024 * blk),
-                                     16, 0, 0);
+    if (u < 2 * NT) {
+      const int bb = 2 * NT * wave + u, brow = 8 * bb + (lane >> 3);
+      const int bchunk = (lane & 7) ^ ((brow ^ (brow >> 3)) & 7);
+      const uint32_t boff = (uint32_t)(brow * kb + 16 * bchunk);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(b0 + boff), (lds_void_t*)(buf + L::kOffB + 1024 * bb),
+                                       16, 0, 0);
+    }
   }
-  const uint8_t* as0 = g.a_scales + m0 * ks + k0 / 16;
-  const uint8_t* bs0 = g.b_scales + n0 * ks + k0 / 16;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int slot = 256 * v + 64 * wave + lane;
-    const int q = slot & 1, i = (slot >> 1) & 3, r = (slot >> 3) & 31, w = (slot >> 8) & 1, gg = slot >> 9;
-    const int row = 128 * w + 32 * i + r;
-    const uint32_t off = (uint32_t)(row * ks + 4 * (2 * gg + q));
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(as0 + off),
-                                     (lds_void_t*)(buf + kDirOffAS + 1024 * v + 256 * wave), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(bs0 + off),
-                                     (lds_void_t*)(buf + kDirOffBS + 1024 * v + 256 * wave), 4, 0, 0);
-  }
+  m32_issue_scales<4>(g.a_scales + m0 * ks + k0 / 16, ks, buf + L::kOffAS);
+  m32_issue_scales<NT>(g.b_scales + n0 * ks + k0 / 16, ks, buf + L::kOffBS);
 }
 
+template <int NT>
 __device__ __forceinline__ void m32_read_scales(const uint8_t* buf, int wm, int wn, int r, int gq,
-                                                M32Scales& d) {
-  const uint4* pa = reinterpret_cast<const uint4*>(buf + kDirOffAS + 32 * ((2 * gq + wm) * 32 + r));
-  const uint4* pb = reinterpret_cast<const uint4*>(buf + kDirOffBS + 32 * ((2 * gq + wn) * 32 + r));
-  d.a[0] = pa[0]; d.a[1] = pa[1]; d.b[0] = pb[0]; d.b[1] = pb[1];
+                                                M32Scales<NT>& d) {
+  using L = M32<NT>;
+  const uint4* pa = reinterpret_cast<const uint4*>(buf + L::kOffAS + 32 * ((2 * gq + wm) * 32 + r));
+  const uint4* pb = reinterpret_cast<const uint4*>(buf + L::kOffBS + 8 * NT * ((2 * gq + wn) * 32 + r));
+  d.a[0] = pa[0];
+  d.a[1] = pa[1];
+#pragma unroll
+  for (int k = 0; k < (NT + 1) / 2; ++k) d.b[k] = pb[k];
 }
 
-// raw codes of block 8g + p for the lane's four A and four B rows
-template <int P>
-__device__ __forceinline__ void m32_read_raw(const uint8_t* buf, int wm, int wn, int r, int gq, M32Raw& q) {
+// raw codes of block 8g + p for the lane's four A and NT B rows
+template <int P, int NT>
+__device__ __forceinline__ void m32_read_raw(const uint8_t* buf, int wm, int wn, int r, int gq,
+                                             M32Raw<NT>& q) {
   const int c = 4 * gq + (P >> 1), sub = 8 * (P & 1);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     q.a[i] = *reinterpret_cast<const uint2*>(buf + dswz(wm * 128 + i * 32 + r, c) + sub);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    q.b[j] = *reinterpret_cast<const uint2*>(buf + kDirOffB + dswz(wn * 128 + j * 32 + r, c) + sub);
+  for (int j = 0; j < NT; ++j)
+    q.b[j] = *reinterpret_cast<const uint2*>(buf + M32<NT>::kOffB + dswz(wn * 32 * NT + j * 32 + r, c) + sub);
 }
 
 __device__ __forceinline__ uint32_t m32_dword(const uint4& v0, const uint4& v1, int k) {
@@ -361,125 +390,138 @@ __device__ __forceinline__ uint32_t m32_dword(const uint4& v0, const uint4& v1, 
 }
 
 // step (P, S): half S of block 8g + P
-template <int P, int S>
-__device__ __forceinline__ void m32_unpack(const M32Raw& q, const M32Scales& d, M32Frag& f) {
+template <int P, int S, int NT>
+__device__ __forceinline__ void m32_unpack(const M32Raw<NT>& q, const M32Scales<NT>& d, M32Frag<NT>& f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     f.a[i] = unpack8(S ? q.a[i].y : q.a[i].x,
                      scale_h2(m32_dword(d.a[0], d.a[1], 2 * i + (P >> 2)) >> (8 * (P & 3))));
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < NT; ++j)
     f.b[j] = unpack8(S ? q.b[j].y : q.b[j].x,
-                     scale_h2(m32_dword(d.b[0], d.b[1], 2 * j + (P >> 2)) >> (8 * (P & 3))));
+                     scale_h2(m32_dword(d.b[0], d.b[(NT + 1) / 2 - 1], 2 * j + (P >> 2)) >> (8 * (P & 3))));
 }
 
-__device__ __forceinline__ void m32_mfma(const M32Frag& f, floatx16 (&acc)[4][4]) {
+template <int NT>
+__device__ __forceinline__ void m32_mfma(const M32Frag<NT>& f, floatx16 (&acc)[4][NT]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NT; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// Instruction order of one step: 16 MFMAs; READS LDS reads ride on the
-// first MFMAs; with DEP the unpack waits on them behind a few MFMAs.
-template <int READS, bool DEP>
+// Instruction order of one step of 4 NT MFMAs; READS groups of LDS reads ride
+// on the first MFMAs; with DEP the unpack waits on them behind a few MFMAs.
+// A step's unpack is about 10 VALU per fragment (4 + NT fragments).
+template <int READS, bool DEP, int NT>
 __device__ __forceinline__ void m32_order() {
+  constexpr int kMfma = 4 * NT;
 #pragma unroll
   for (int k = 0; k < READS; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, DEP ? 2 : 1, 0);
     if (!DEP) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
   }
-  constexpr int kCover = DEP ? 3 : 0;
+  constexpr int kCover = DEP ? (NT == 4 ? 3 : 2) : 0;
 #pragma unroll
   for (int k = 0; k < kCover; ++k) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  constexpr int kRest = 16 - READS - kCover;
+  constexpr int kRest = kMfma - READS - kCover;
+  constexpr int kValu = NT == 4 ? (DEP ? 8 : 6) : (DEP ? 14 : 9);
 #pragma unroll
   for (int k = 0; k < kRest; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, DEP ? 8 : 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
   }
 }
 
 // pair P of a stage: steps 2P and 2P + 1.  In: f = step (P, 0), q = raw P.
-template <int P>
-__device__ __forceinline__ void m32_pair(const uint8_t* cur, M32Frag& f, M32Raw& q, const M32Scales& d,
-                                         floatx16 (&acc)[4][4], int wm, int wn, int r, int gq) {
-  M32Frag f1;
-  M32Raw qn;
-  m32_mfma(f, acc);
-  m32_read_raw<P + 1>(cur, wm, wn, r, gq, qn);
-  m32_unpack<P, 1>(q, d, f1);
-  m32_order<8, false>();
+template <int P, int NT>
+__device__ __forceinline__ void m32_pair(const uint8_t* cur, M32Frag<NT>& f, M32Raw<NT>& q,
+                                         const M32Scales<NT>& d, floatx16 (&acc)[4][NT], int wm, int wn,
+                                         int r, int gq) {
+  M32Frag<NT> f1;
+  M32Raw<NT> qn;
+  m32_mfma<NT>(f, acc);
+  m32_read_raw<P + 1, NT>(cur, wm, wn, r, gq, qn);
+  m32_unpack<P, 1, NT>(q, d, f1);
+  m32_order<4 + NT, false, NT>();
   __builtin_amdgcn_sched_barrier(0);
-  m32_mfma(f1, acc);
-  m32_unpack<P + 1, 0>(qn, d, f);
-  m32_order<0, false>();
+  m32_mfma<NT>(f1, acc);
+  m32_unpack<P + 1, 0, NT>(qn, d, f);
+  m32_order<0, false, NT>();
   __builtin_amdgcn_sched_barrier(0);
   q = qn;
 }
 
 // One stage from cur.  In: f = step (0, 0), q = raw 0, d = scales.  Out: the
-// same for the stage in nxt; after the barrier, when issue is set, stage
-// k_issue streams into cur (every wave is done reading it).
+// same for the stage in nxt; after the barrier, when issue is set, the stage
+// at (m0, n0, k_issue) streams into cur (every wave is done reading it).
+template <int NT>
 __device__ __forceinline__ void m32_stage(const GemmArgs& g, int64_t m0, int64_t n0, bool issue,
-                                          int64_t k_issue, uint8_t* cur, const uint8_t* nxt, M32Frag& f,
-                                          M32Raw& q, M32Scales& d, floatx16 (&acc)[4][4], int wm, int wn,
-                                          int r, int gq) {
-  m32_pair<0>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<1>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<2>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<3>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<4>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<5>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<6>(cur, f, q, d, acc, wm, wn, r, gq);
-  M32Frag f1;
-  m32_mfma(f, acc);
-  m32_unpack<7, 1>(q, d, f1);
-  m32_order<0, false>();
+                                          int64_t k_issue, uint8_t* cur, const uint8_t* nxt, M32Frag<NT>& f,
+                                          M32Raw<NT>& q, M32Scales<NT>& d, floatx16 (&acc)[4][NT], int wm,
+                                          int wn, int r, int gq) {
+  m32_pair<0, NT>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<1, NT>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<2, NT>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<3, NT>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<4, NT>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<5, NT>(cur, f, q, d, acc, wm, wn, r, gq);
+  m32_pair<6, NT>(cur, f, q, d, acc, wm, wn, r, gq);
+  M32Frag<NT> f1;
+  m32_mfma<NT>(f, acc);
+  m32_unpack<7, 1, NT>(q, d, f1);
+  m32_order<0, false, NT>();
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // waits for this wave's loads of nxt (vmcnt(0)), then all waves
-  if (issue) m32_issue(g, m0, n0, k_issue, cur);
+  if (issue) m32_issue<NT>(g, m0, n0, k_issue, cur);
   __builtin_amdgcn_sched_barrier(0);
-  m32_mfma(f1, acc);
-  m32_read_scales(nxt, wm, wn, r, gq, d);
-  m32_read_raw<0>(nxt, wm, wn, r, gq, q);
-  m32_unpack<0, 0>(q, d, f);
-  m32_order<6, true>();
+  m32_mfma<NT>(f1, acc);
+  m32_read_scales<NT>(nxt, wm, wn, r, gq, d);
+  m32_read_raw<0, NT>(nxt, wm, wn, r, gq, q);
+  m32_unpack<0, 0, NT>(q, d, f);
+  m32_order<NT == 4 ? 6 : 5, true, NT>();
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g) {
-  __shared__ __align__(16) uint8_t buf0[kDirStage];
-  __shared__ __align__(16) uint8_t buf1[kDirStage];
-  const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * 256;
+// Workgroup u computes columns (u % (4 / NT)) * 64 NT .. of the 256 x 256
+// tile tile0 + u / (4 / NT) (tiles in row-major order, N / 256 per row).
+template <int NT>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_t tile0) {
+  using L = M32<NT>;
+  __shared__ __align__(16) uint8_t buf0[L::kStage];
+  __shared__ __align__(16) uint8_t buf1[L::kStage];
+  constexpr int kSub = 4 / NT;
+  const int64_t ntn = g.N / 256;
+  const int64_t t = tile0 + blockIdx.x / kSub;
+  const int64_t m0 = (t / ntn) * 256, n0 = (t % ntn) * 256 + (blockIdx.x % kSub) * L::kBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, gq = lane >> 5;
 
-  floatx16 acc[4][4];
+  floatx16 acc[4][NT];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int k = 0; k < 16; ++k) acc[i][j][k] = 0.f;
 
   const int64_t nk = g.K / kDirBK;  // even
-  m32_issue(g, m0, n0, 0, buf0);
+  m32_issue<NT>(g, m0, n0, 0, buf0);
   __syncthreads();
-  m32_issue(g, m0, n0, kDirBK, buf1);
-  M32Frag f;
-  M32Raw q;
-  M32Scales d;
-  m32_read_scales(buf0, wm, wn, r, gq, d);
-  m32_read_raw<0>(buf0, wm, wn, r, gq, q);
-  m32_unpack<0, 0>(q, d, f);
+  m32_issue<NT>(g, m0, n0, kDirBK, buf1);
+  M32Frag<NT> f;
+  M32Raw<NT> q;
+  M32Scales<NT> d;
+  m32_read_scales<NT>(buf0, wm, wn, r, gq, d);
+  m32_read_raw<0, NT>(buf0, wm, wn, r, gq, q);
+  m32_unpack<0, 0, NT>(q, d, f);
   for (int64_t kt = 0; kt < nk; kt += 2) {
-    m32_stage(g, m0, n0, kt + 2 < nk, (kt + 2) * kDirBK, buf0, buf1, f, q, d, acc, wm, wn, r, gq);
+    m32_stage<NT>(g, m0, n0, kt + 2 < nk, (kt + 2) * kDirBK, buf0, buf1, f, q, d, acc, wm, wn, r, gq);
     // on the last stage the reads of buf0 at its end are of stale data and unused
-    m32_stage(g, m0, n0, kt + 3 < nk, (kt + 3) * kDirBK, buf1, buf0, f, q, d, acc, wm, wn, r, gq);
+    m32_stage<NT>(g, m0, n0, kt + 3 < nk, (kt + 3) * kDirBK, buf1, buf0, f, q, d, acc, wm, wn, r, gq);
   }
 
   // D layout of the 32 x 32 MFMA: lane l, value k -> column l % 32, row
@@ -488,8 +530,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 128 + j * 32 + r;
+    for (int j = 0; j < NT; ++j) {
+      const int64_t n = n0 + wn * 32 * NT + j * 32 + r;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int64_t m = m0 + wm * 128 + i * 32 + 8 * (k >> 2) + 4 * gq + (k & 3);
@@ -500,19 +542,31 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g) {
 }
 
 void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
-  (void)cus;
   constexpr int BM = 256, BN = 256;
   const dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM));
   const bool aligned = g.K % kBK == 0 && ((uintptr_t)g.a_codes % 16 == 0) &&
                        ((uintptr_t)g.b_codes % 16 == 0) && ((uintptr_t)g.a_scales % 8 == 0) &&
                        ((uintptr_t)g.b_scales % 8 == 0);
   if (aligned && g.M % 256 == 0 && g.N % 256 == 0 && g.K % (2 * kDirBK) == 0 &&
-      g.K <= (INT64_C(1) << 26) && (uintptr_t)g.a_scales % 4 == 0 && (uintptr_t)g.b_scales % 4 == 0)
-    hipLaunchKernelGGL(k_gemm_m32, grid, dim3(kGemmThreads), 0, st, g);
-  else if (aligned)
+      g.K <= (INT64_C(1) << 26) && (uintptr_t)g.a_scales % 4 == 0 && (uintptr_t)g.b_scales % 4 == 0) {
+    // Whole waves of 256 x 256 tiles (one workgroup per CU); when the last
+    // wave would be at most half full, its tiles run as 256 x 128 halves
+    // instead, so that wave takes about half as long.
+    const int64_t ntiles = (g.M / 256) * (g.N / 256);
+    const int64_t c = std::max(cus, 1);
+    const int64_t full = (ntiles / c) * c, rem = ntiles - full;
+    if (rem == 0 || 2 * rem > c) {
+      hipLaunchKernelGGL(k_gemm_m32<4>, dim3((unsigned)ntiles), dim3(kGemmThreads), 0, st, g, INT64_C(0));
+    } else {
+      if (full > 0)
+        hipLaunchKernelGGL(k_gemm_m32<4>, dim3((unsigned)full), dim3(kGemmThreads), 0, st, g, INT64_C(0));
+      hipLaunchKernelGGL(k_gemm_m32<2>, dim3((unsigned)(2 * rem)), dim3(kGemmThreads), 0, st, g, full);
+    }
+  } else if (aligned) {
     hipLaunchKernelGGL((k_gemm<BM, BN, true>), grid, dim3(kGemmThreads), 0, st, g);
-  else
+  } else {
     hipLaunchKernelGGL((k_gemm<BM, BN, false>), grid, dim3(kGemmThreads), 0, st, g);
+  }
 }
 
 }  // namespace nvfp4
