@@ -306,7 +306,7 @@ struct M32 {
 template <int NT>
 struct M32Frag { half8 a[4], b[NT]; };
 template <int NT>
-struct M32Raw { uint2 a[4], b[NT]; };
+struct M32Raw { uint4 a[4], b[NT]; };  // blocks 8g + 2Q (.x, .y) and 8g + 2Q + 1 (.z, .w)
 template <int NT>
 struct M32Scales { uint4 a[2], b[(NT + 1) / 2]; };  // dword 2i + q: blocks 8g + 4q .. + 3 of tile-row i
 
@@ -371,17 +371,22 @@ __device__ __forceinline__ void m32_read_scales(const uint8_t* buf, int wm, int 
   for (int k = 0; k < (NT + 1) / 2; ++k) d.b[k] = pb[k];
 }
 
-// raw codes of block 8g + p for the lane's four A and NT B rows
-template <int P, int NT>
+// raw codes of blocks 8g + 2Q and 8g + 2Q + 1 (one 16-byte chunk) for the
+// lane's four A and NT B rows; the eight rows of a swizzle group hit eight
+// distinct chunk positions, so a 16-byte read is free of bank conflicts
+template <int Q, int NT>
 __device__ __forceinline__ void m32_read_raw(const uint8_t* buf, int wm, int wn, int r, int gq,
                                              M32Raw<NT>& q) {
-  const int c = 4 * gq + (P >> 1), sub = 8 * (P & 1);
+  const int c = 4 * gq + Q;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    q.a[i] = *reinterpret_cast<const uint2*>(buf + dswz(wm * 128 + i * 32 + r, c) + sub);
+  for (int i = 0; i < 4; ++i) q.a[i] = *reinterpret_cast<const uint4*>(buf + dswz(wm * 128 + i * 32 + r, c));
 #pragma unroll
   for (int j = 0; j < NT; ++j)
-    q.b[j] = *reinterpret_cast<const uint2*>(buf + M32<NT>::kOffB + dswz(wn * 32 * NT + j * 32 + r, c) + sub);
+    q.b[j] = *reinterpret_cast<const uint4*>(buf + M32<NT>::kOffB + dswz(wn * 32 * NT + j * 32 + r, c));
+}
+
+__device__ __forceinline__ uint32_t raw_word(const uint4& v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
 __device__ __forceinline__ uint32_t m32_dword(const uint4& v0, const uint4& v1, int k) {
@@ -392,13 +397,14 @@ __device__ __forceinline__ uint32_t m32_dword(const uint4& v0, const uint4& v1, 
 // step (P, S): half S of block 8g + P
 template <int P, int S, int NT>
 __device__ __forceinline__ void m32_unpack(const M32Raw<NT>& q, const M32Scales<NT>& d, M32Frag<NT>& f) {
+  constexpr int kw = 2 * (P & 1) + S;  // word of the 16-byte chunk
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    f.a[i] = unpack8(S ? q.a[i].y : q.a[i].x,
+    f.a[i] = unpack8(raw_word(q.a[i], kw),
                      scale_h2(m32_dword(d.a[0], d.a[1], 2 * i + (P >> 2)) >> (8 * (P & 3))));
 #pragma unroll
   for (int j = 0; j < NT; ++j)
-    f.b[j] = unpack8(S ? q.b[j].y : q.b[j].x,
+    f.b[j] = unpack8(raw_word(q.b[j], kw),
                      scale_h2(m32_dword(d.b[0], d.b[(NT + 1) / 2 - 1], 2 * j + (P >> 2)) >> (8 * (P & 3))));
 }
 
@@ -435,23 +441,29 @@ __device__ __forceinline__ void m32_order() {
   }
 }
 
-// pair P of a stage: steps 2P and 2P + 1.  In: f = step (P, 0), q = raw P.
+// pair P of a stage: steps 2P and 2P + 1.  In: f = step (P, 0), q = raw of
+// quad P / 2 (pairs P & ~1 and P | 1).  An even pair also reads the next
+// quad into qn; an odd pair hands it over.
 template <int P, int NT>
-__device__ __forceinline__ void m32_pair(const uint8_t* cur, M32Frag<NT>& f, M32Raw<NT>& q,
+__device__ __forceinline__ void m32_pair(const uint8_t* cur, M32Frag<NT>& f, M32Raw<NT>& q, M32Raw<NT>& qn,
                                          const M32Scales<NT>& d, floatx16 (&acc)[4][NT], int wm, int wn,
                                          int r, int gq) {
+  constexpr bool kRead = (P & 1) == 0 && P < 6;
   M32Frag<NT> f1;
-  M32Raw<NT> qn;
   m32_mfma<NT>(f, acc);
-  m32_read_raw<P + 1, NT>(cur, wm, wn, r, gq, qn);
+  if (kRead) m32_read_raw<P / 2 + 1, NT>(cur, wm, wn, r, gq, qn);
   m32_unpack<P, 1, NT>(q, d, f1);
-  m32_order<4 + NT, false, NT>();
+  m32_order<kRead ? 4 + NT : 0, false, NT>();
   __builtin_amdgcn_sched_barrier(0);
   m32_mfma<NT>(f1, acc);
-  m32_unpack<P + 1, 0, NT>(qn, d, f);
+  if (P & 1) {
+    m32_unpack<P + 1, 0, NT>(qn, d, f);
+    q = qn;
+  } else {
+    m32_unpack<P + 1, 0, NT>(q, d, f);
+  }
   m32_order<0, false, NT>();
   __builtin_amdgcn_sched_barrier(0);
-  q = qn;
 }
 
 // One stage from cur.  In: f = step (0, 0), q = raw 0, d = scales.  Out: the
@@ -462,13 +474,14 @@ __device__ __forceinline__ void m32_stage(const GemmArgs& g, int64_t m0, int64_t
                                           int64_t k_issue, uint8_t* cur, const uint8_t* nxt, M32Frag<NT>& f,
                                           M32Raw<NT>& q, M32Scales<NT>& d, floatx16 (&acc)[4][NT], int wm,
                                           int wn, int r, int gq) {
-  m32_pair<0, NT>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<1, NT>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<2, NT>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<3, NT>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<4, NT>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<5, NT>(cur, f, q, d, acc, wm, wn, r, gq);
-  m32_pair<6, NT>(cur, f, q, d, acc, wm, wn, r, gq);
+  M32Raw<NT> qn;
+  m32_pair<0, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
+  m32_pair<1, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
+  m32_pair<2, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
+  m32_pair<3, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
+  m32_pair<4, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
+  m32_pair<5, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
+  m32_pair<6, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
   M32Frag<NT> f1;
   m32_mfma<NT>(f, acc);
   m32_unpack<7, 1, NT>(q, d, f1);
