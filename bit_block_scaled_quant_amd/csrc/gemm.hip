@@ -433,7 +433,7 @@ __device__ __forceinline__ void m32_order() {
 #pragma unroll
   for (int k = 0; k < kCover; ++k) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   constexpr int kRest = kMfma - READS - kCover;
-  constexpr int kValu = NT == 4 ? (DEP ? 8 : 6) : (DEP ? 14 : 9);
+  constexpr int kValu = NT == 4 ? (DEP ? 8 : 5) : (DEP ? 14 : 7);  // group sizes tuned by measurement
 #pragma unroll
   for (int k = 0; k < kRest; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
