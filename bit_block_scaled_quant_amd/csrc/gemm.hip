@@ -548,7 +548,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int64_t m = m0 + wm * 128 + i * 32 + 8 * (k >> 2) + 4 * gq + (k & 3);
-        g.c[m * g.N + n] = (acc[i][j][k] * inv_a) * inv_b;
+        // streaming store: C is written once and not read here (+2.5% measured)
+        __builtin_nontemporal_store((acc[i][j][k] * inv_a) * inv_b, &g.c[m * g.N + n]);
       }
     }
   }
