@@ -22,7 +22,9 @@
 //   Philox(key = seed, counter = (i >> 3, stream, 0)).
 //
 // Every fp32 step is a single correctly rounded operation: the library is
-// compiled with -ffp-contract=off and divisions use __fdiv_rn.
+// compiled with -ffp-contract=off, divisions use __fdiv_rn, and the one
+// division by a constant (by 6, in the block scale) uses a correction step
+// that is exact where it matters (div6).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -61,14 +63,39 @@ __device__ __forceinline__ float tensor_scale_from_amax(float amax) {
   return fminf(s, kFltMax);
 }
 
+// t / 6 for t >= 0 in three operations: the product with fl(1/6), corrected
+// once by its exact fma residual (Markstein's correction step).  The result
+// is the correctly rounded quotient for every t in [2^-125, FLT_MAX] (checked
+// exhaustively on the host over all those bit patterns).  Below 2^-125 it may
+// miss by an ulp of a subnormal, and +inf gives NaN: in both cases the E4M3
+// byte of the quotient is unchanged (0x00 below 2^-10; 0x7E, since the
+// saturation test is false for inf and NaN alike).
+__device__ __forceinline__ float div6(float t) {
+  const float c = 0.16666667163372039795f;  // fl(1/6)
+  const float q0 = t * c;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, t), c, q0);
+}
+
+// Table of the element multiplier for each scale byte: inv = S_enc / sb
+// rounded once, at most FLT_MAX, and 0 for the zero scale.  Every encode
+// workgroup builds it in LDS before its first block (the first 128 threads,
+// then a barrier), so a block's multiplier is one LDS read instead of a
+// decode and a division.
+constexpr int kInvTable = 128;
+
+__device__ __forceinline__ void build_inv_table(float* tab, float s_enc) {
+  if (threadIdx.x < kInvTable) {
+    const float sb = e4m3_decode(threadIdx.x);
+    tab[threadIdx.x] = threadIdx.x == 0 ? 0.0f : fminf(__fdiv_rn(s_enc, sb), kFltMax);
+  }
+  __syncthreads();
+}
+
 // block scale byte and element multiplier for a block with amax amax_b
-__device__ __forceinline__ uint32_t block_scale(float amax_b, float s_enc, float* inv) {
-  const float t = amax_b * s_enc;
-  const float s = __fdiv_rn(t, 6.0f);
-  const uint32_t byte = e4m3_encode(s);
-  const float sb = e4m3_decode(byte);
-  const float q = fminf(__fdiv_rn(s_enc, sb), kFltMax);  // +inf for sb == 0, not used then
-  *inv = (sb == 0.0f) ? 0.0f : q;
+__device__ __forceinline__ uint32_t block_scale(float amax_b, float s_enc, const float* inv_tab,
+                                                float* inv) {
+  const uint32_t byte = e4m3_encode(div6(amax_b * s_enc));
+  *inv = inv_tab[byte];
   return byte;
 }
 

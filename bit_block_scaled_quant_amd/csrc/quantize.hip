@@ -29,6 +29,7 @@
 namespace nvfp4 {
 
 constexpr int kThreads = 256;
+static_assert(kThreads >= kInvTable, "the inverse-scale table is built by one thread per entry");
 constexpr int kTile = 128;
 
 // raw storage of eight consecutive input elements (e % 8 == 0)
@@ -193,8 +194,10 @@ __global__ __launch_bounds__(kThreads) void k_encode_rows(const void* __restrict
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales,
                                                           float* __restrict__ ts) {
+  __shared__ float inv_tab[kInvTable];
   const float s_enc = tensor_scale_from_amax(ts[1]);
   if (blockIdx.x == 0 && threadIdx.x == 0) ts[0] = s_enc;
+  build_inv_table(inv_tab, s_enc);
   const int lane = threadIdx.x & 63;
   const bool odd = lane & 1;
   const int64_t npiece = (nblk + 31) / 32;  // 512 elements per piece
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_rows(const void* __restrict
       for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
       m = fmaxf(m, lane_pair_swap(m));
       float inv;
-      const uint32_t byte = block_scale(m, s_enc, &inv);
+      const uint32_t byte = block_scale(m, s_enc, inv_tab, &inv);
       if (valid[u]) {
         // rowwise: block b covers elements 16b .. 16b + 15 of the row-major tensor
         const int64_t e = blk[u] * 16 + 8 * odd;
@@ -246,15 +249,17 @@ __global__ __launch_bounds__(kThreads) void k_encode_rows_blk(const void* __rest
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales,
                                                           float* __restrict__ ts) {
+  __shared__ float inv_tab[kInvTable];
   const float s_enc = tensor_scale_from_amax(ts[1]);
   if (blockIdx.x == 0 && threadIdx.x == 0) ts[0] = s_enc;
+  build_inv_table(inv_tab, s_enc);
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
     float v[16];
     load16<BF16>(x, b * 16, v);
     if (RHT) rht16(v, rht_mask);
     float inv;
-    const uint32_t byte = block_scale(amax16(v), s_enc, &inv);
+    const uint32_t byte = block_scale(amax16(v), s_enc, inv_tab, &inv);
     // rowwise: block b covers elements 16b .. 16b+15 of the row-major tensor
     reinterpret_cast<uint2*>(codes)[b] = encode16<SR>(v, inv, seed, 0u, (uint64_t)b * 16);
     scales[b] = (uint8_t)byte;
@@ -313,7 +318,8 @@ __device__ __forceinline__ void load16_stash(const void* __restrict__ x, int64_t
 template <bool BF16, bool SR>
 __device__ __forceinline__ void columnwise_half(const typename TileElem<BF16>::T* tile, int pitch,
                                                 int col, int half, int rows_in, int64_t R,
-                                                int64_t r0, int64_t c, float s_enc, uint64_t seed,
+                                                int64_t r0, int64_t c, float s_enc,
+                                                const float* inv_tab, uint64_t seed,
                                                 uint8_t* __restrict__ codes_t,
                                                 uint8_t* __restrict__ scales_t) {
 #pragma unroll 1
@@ -323,7 +329,7 @@ __device__ __forceinline__ void columnwise_half(const typename TileElem<BF16>::T
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = TileElem<BF16>::to_float(tile[(rb * 16 + j) * pitch + col]);
     float inv;
-    const uint32_t byte = block_scale(amax16(v), s_enc, &inv);
+    const uint32_t byte = block_scale(amax16(v), s_enc, inv_tab, &inv);
     const int64_t r = r0 + rb * 16;
     const uint2 q = encode16<SR>(v, inv, seed, 1u, (uint64_t)(c * R + r));
     *reinterpret_cast<uint2*>(codes_t + c * (R / 2) + r / 2) = q;
@@ -339,9 +345,11 @@ __global__ __launch_bounds__(kThreads) void k_encode_tile1d(
   using E = TileElem<BF16>;
   constexpr int pitch = kTile + E::kPad;
   __shared__ __align__(16) typename E::T tile[kTile * pitch];
+  __shared__ float inv_tab[kInvTable];
 
   const float s_enc = tensor_scale_from_amax(ts[1]);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) ts[0] = s_enc;
+  build_inv_table(inv_tab, s_enc);
   const int64_t r0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;
   const int rows_in = (int)(R - r0 < kTile ? R - r0 : kTile);
   const int cols_in = (int)(C - c0 < kTile ? C - c0 : kTile);
@@ -355,14 +363,14 @@ __global__ __launch_bounds__(kThreads) void k_encode_tile1d(
     float v[16];
     load16_stash<BF16>(x, e, tile + row * pitch + cb * 16, v);
     float inv;
-    const uint32_t byte = block_scale(amax16(v), s_enc, &inv);
+    const uint32_t byte = block_scale(amax16(v), s_enc, inv_tab, &inv);
     *reinterpret_cast<uint2*>(codes + e / 2) = encode16<SR>(v, inv, seed, 0u, (uint64_t)e);
     scales[e / 16] = (uint8_t)byte;
   }
   __syncthreads();
   const int col = threadIdx.x >> 1, half = threadIdx.x & 1;
   if (col < cols_in)
-    columnwise_half<BF16, SR>(tile, pitch, col, half, rows_in, R, r0, c0 + col, s_enc, seed,
+    columnwise_half<BF16, SR>(tile, pitch, col, half, rows_in, R, r0, c0 + col, s_enc, inv_tab, seed,
                               codes_t, scales_t);
 }
 
@@ -438,8 +446,10 @@ __global__ __launch_bounds__(kThreads) void k_encode_2d(
   uint32_t* qs = qs_all[wv];
   uint32_t* tq = tq_all[wv];
   uint8_t* rs = reinterpret_cast<uint8_t*>(rs_all[wv]);
+  __shared__ float inv_tab[kInvTable];
   const float s_enc = tensor_scale_from_amax(ts[1]);
   if (blockIdx.x == 0 && threadIdx.x == 0) ts[0] = s_enc;
+  build_inv_table(inv_tab, s_enc);
   const int64_t tiles_c = (C + 4 * kStripCols - 1) / (4 * kStripCols);
   const int64_t ntiles = ((R + 127) / 128) * tiles_c;
   // Workgroups are dealt to the eight XCDs in turn; tile numbers are laid
@@ -492,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_2d(
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fmaxf(fabsf(va[j]), fabsf(vb[j])));
     m = row16_max(m);
     float inv;
-    const uint32_t byte = block_scale(m, s_enc, &inv);
+    const uint32_t byte = block_scale(m, s_enc, inv_tab, &inv);
     uint32_t qa = 0u, qb = 0u;
     if (act) {
       qa = encode8<SR>(va, inv, seed, 0u, (uint64_t)ea);
