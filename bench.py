@@ -10,6 +10,10 @@ Language Models with NVFP4", sections 2B and 3):
          using W's transposed copy
   wgrad  quantize dY^T [20480x8192] (1D, SR, RHT) and X^T [5120x8192] (1D, RNE,
          RHT); dW = dY^T . X                              (20480, 5120, 8192)
+By default X and X^T come from one cast-transpose call on X, and dY and dY^T
+from one on dY (nvfp4_quantize_cast_transpose: bit-identical to the separate
+calls, without a transposed bf16 copy of X or dY).  --composed times the
+five separate quantize calls instead, on transposes made before the timing.
 value = GEMM flops of the step (3 x 2MNK) / wall time of the step, quantizers
 included.  Per-call times come from HIP events on the launch stream.
 
@@ -41,6 +45,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--composed", action="store_true",
+                   help="quantize X^T and dY^T by separate calls on materialized transposes "
+                        "instead of the cast-transpose")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 256 MiB device copy three times (for scaling the "
                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -155,8 +162,9 @@ def main():
     X = datagen.act(dev, seed=seed)
     W = datagen.weight(dev, seed=seed)
     dY = datagen.grad(dev, seed=seed)
-    dYt = dY.t().contiguous()
-    Xt = X.t().contiguous()
+    if args.composed:
+        dYt = dY.t().contiguous()
+        Xt = X.t().contiguous()
     torch.cuda.synchronize()
 
     def alloc(rows, cols, transposed):
@@ -178,26 +186,42 @@ def main():
     dW = torch.empty(FFN, HIDDEN, dtype=torch.float32, device=dev)
     qWt = nv.Quantized(qW.codes_t, qW.scales_t, qW.tensor_scale)
 
-    calls = [
-        ("quant_X_1d_rne", "quant", lambda: nv.nvfp4_quantize(X, 0, 0, 0, 0, qX.codes, qX.scales,
-                                                              qX.tensor_scale),
-         quant_bytes(TOKENS, HIDDEN, 2, False)),
-        ("quant_W_2d_rne_t", "quant", lambda: nv.nvfp4_quantize_2d(
-            W, 0, 0, qW.codes, qW.scales, qW.tensor_scale, qW.codes_t, qW.scales_t),
-         quant_bytes(FFN, HIDDEN, 2, True)),
-        ("gemm_fprop", "gemm", lambda: nv.gemm(qX, qW, out=Y), (TOKENS, FFN, HIDDEN)),
-        ("quant_dY_1d_sr", "quant", lambda: nv.nvfp4_quantize(dY, 1, seed, 0, 0, qdY.codes,
-                                                              qdY.scales, qdY.tensor_scale),
-         quant_bytes(TOKENS, FFN, 2, False)),
-        ("gemm_dgrad", "gemm", lambda: nv.gemm(qdY, qWt, out=dX), (TOKENS, HIDDEN, FFN)),
-        ("quant_dYt_1d_sr_rht", "quant", lambda: nv.nvfp4_quantize(
-            dYt, 1, seed, 1, seed, qdYt.codes, qdYt.scales, qdYt.tensor_scale),
-         quant_bytes(FFN, TOKENS, 2, False)),
-        ("quant_Xt_1d_rne_rht", "quant", lambda: nv.nvfp4_quantize(
-            Xt, 0, 0, 1, seed, qXt.codes, qXt.scales, qXt.tensor_scale),
-         quant_bytes(HIDDEN, TOKENS, 2, False)),
-        ("gemm_wgrad", "gemm", lambda: nv.gemm(qdYt, qXt, out=dW), (FFN, HIDDEN, TOKENS)),
-    ]
+    quant_W = ("quant_W_2d_rne_t", "quant", lambda: nv.nvfp4_quantize_2d(
+        W, 0, 0, qW.codes, qW.scales, qW.tensor_scale, qW.codes_t, qW.scales_t),
+        quant_bytes(FFN, HIDDEN, 2, True))
+    gemm_fprop = ("gemm_fprop", "gemm", lambda: nv.gemm(qX, qW, out=Y), (TOKENS, FFN, HIDDEN))
+    gemm_dgrad = ("gemm_dgrad", "gemm", lambda: nv.gemm(qdY, qWt, out=dX), (TOKENS, HIDDEN, FFN))
+    gemm_wgrad = ("gemm_wgrad", "gemm", lambda: nv.gemm(qdYt, qXt, out=dW), (FFN, HIDDEN, TOKENS))
+    if args.composed:
+        calls = [
+            ("quant_X_1d_rne", "quant", lambda: nv.nvfp4_quantize(X, 0, 0, 0, 0, qX.codes, qX.scales,
+                                                                  qX.tensor_scale),
+             quant_bytes(TOKENS, HIDDEN, 2, False)),
+            quant_W, gemm_fprop,
+            ("quant_dY_1d_sr", "quant", lambda: nv.nvfp4_quantize(dY, 1, seed, 0, 0, qdY.codes,
+                                                                  qdY.scales, qdY.tensor_scale),
+             quant_bytes(TOKENS, FFN, 2, False)),
+            gemm_dgrad,
+            ("quant_dYt_1d_sr_rht", "quant", lambda: nv.nvfp4_quantize(
+                dYt, 1, seed, 1, seed, qdYt.codes, qdYt.scales, qdYt.tensor_scale),
+             quant_bytes(FFN, TOKENS, 2, False)),
+            ("quant_Xt_1d_rne_rht", "quant", lambda: nv.nvfp4_quantize(
+                Xt, 0, 0, 1, seed, qXt.codes, qXt.scales, qXt.tensor_scale),
+             quant_bytes(HIDDEN, TOKENS, 2, False)),
+            gemm_wgrad,
+        ]
+    else:
+        # the same outputs as the composed calls (same seeds), bit for bit
+        calls = [
+            ("ct_X_rne_rht", "quant", lambda: nv.nvfp4_quantize_cast_transpose(
+                X, 0, 0, 0, 1, seed, qX.codes, qX.scales, qX.tensor_scale, qXt.codes, qXt.scales,
+                qXt.tensor_scale), quant_bytes(TOKENS, HIDDEN, 2, True)),
+            quant_W, gemm_fprop,
+            ("ct_dY_sr_rht", "quant", lambda: nv.nvfp4_quantize_cast_transpose(
+                dY, 1, seed, seed, 1, seed, qdY.codes, qdY.scales, qdY.tensor_scale, qdYt.codes,
+                qdYt.scales, qdYt.tensor_scale), quant_bytes(TOKENS, FFN, 2, True)),
+            gemm_dgrad, gemm_wgrad,
+        ]
 
     def step(events=None):
         for i, (_, _, fn, _) in enumerate(calls):
@@ -273,6 +297,8 @@ def main():
         "dtype": "nvfp4 operands, fp16 MFMA, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": "12B FFN-up linear layer, NVFP4 fprop+dgrad+wgrad",
+                   "quantizer_calls": "separate (transposes made before timing)" if args.composed
+                   else "cast-transpose for X and dY",
                    "X": [TOKENS, HIDDEN], "W": [FFN, HIDDEN], "dY": [TOKENS, FFN],
                    "gemm_MNK": [[TOKENS, FFN, HIDDEN], [TOKENS, HIDDEN, FFN],
                                 [FFN, HIDDEN, TOKENS]]},

@@ -2,12 +2,14 @@
 
 A thin ctypes binding over ``libnvfp4.so`` (C ABI in ``include/nvfp4.h``).
 The functions named like the C entry points (``nvfp4_quantize``,
-``nvfp4_quantize_2d``, ``nvfp4_rht``, ``nvfp4_gemm``) only marshal torch
+``nvfp4_quantize_2d``, ``nvfp4_quantize_cast_transpose``, ``nvfp4_rht``,
+``nvfp4_gemm``) only marshal torch
 tensors into pointers and the current HIP stream; every step of the
 computation runs in the library's HIP kernels.  There is no CPU fallback: if
 the library is missing, or a tensor is not on the GPU, the call raises.
 
-Convenience wrappers (``quantize``, ``quantize_2d``, ``rht``, ``gemm``)
+Convenience wrappers (``quantize``, ``quantize_2d``,
+``quantize_cast_transpose``, ``rht``, ``gemm``)
 allocate the outputs with torch (device memory only) and call the same
 entry points.
 """
@@ -51,6 +53,9 @@ def lib():
         L.nvfp4_quantize.argtypes = [P, I, I64, I64, I, U64, I, U64, P, P, P, P, P, P]
         L.nvfp4_quantize_2d.restype = I
         L.nvfp4_quantize_2d.argtypes = [P, I, I64, I64, I, U64, P, P, P, P, P, P]
+        L.nvfp4_quantize_cast_transpose.restype = I
+        L.nvfp4_quantize_cast_transpose.argtypes = [P, I, I64, I64, I, U64, U64, I, U64, P, P, P, P, P, P,
+                                                    P]
         L.nvfp4_rht.restype = I
         L.nvfp4_rht.argtypes = [P, I, I64, I64, U64, P, P]
         L.nvfp4_gemm.restype = I
@@ -108,6 +113,15 @@ def nvfp4_quantize_2d(w, rounding, seed, codes, scales, tensor_scale, codes_t=No
                                    _ptr(scales_t), _stream(w)), "nvfp4_quantize_2d")
 
 
+def nvfp4_quantize_cast_transpose(x, rounding, seed, seed_t, rht_t, rht_seed, codes, scales, tensor_scale,
+                                  codes_t, scales_t, tensor_scale_t):
+    rows, cols = x.shape
+    _check(lib().nvfp4_quantize_cast_transpose(
+        _ptr(x), _dtype(x), rows, cols, int(rounding), int(seed), int(seed_t), int(rht_t), int(rht_seed),
+        _ptr(codes), _ptr(scales), _ptr(tensor_scale), _ptr(codes_t), _ptr(scales_t), _ptr(tensor_scale_t),
+        _stream(x)), "nvfp4_quantize_cast_transpose")
+
+
 def nvfp4_rht(x, rht_seed, y):
     rows, cols = x.shape
     _check(lib().nvfp4_rht(_ptr(x), _dtype(x), rows, cols, int(rht_seed), _ptr(y), _stream(x)),
@@ -163,6 +177,18 @@ def quantize_2d(w, rounding=RNE, seed=0, transposed=True) -> Quantized:
     q = _alloc(rows, cols, w.device, transposed)
     nvfp4_quantize_2d(w, rounding, seed, q.codes, q.scales, q.tensor_scale, q.codes_t, q.scales_t)
     return q
+
+
+def quantize_cast_transpose(x, rounding=RNE, seed=0, seed_t=1, rht_t=True, rht_seed=0):
+    """(rowwise, columnwise): the quantization of x [rows][cols] along cols,
+    and that of x^T [cols][rows] (with the Hadamard transform when rht_t),
+    each with its own tensor scale, from one cast-transpose call."""
+    rows, cols = x.shape
+    q = _alloc(rows, cols, x.device, False)
+    qt = _alloc(cols, rows, x.device, False)
+    nvfp4_quantize_cast_transpose(x, rounding, seed, seed_t, int(rht_t), rht_seed, q.codes, q.scales,
+                                  q.tensor_scale, qt.codes, qt.scales, qt.tensor_scale)
+    return q, qt
 
 
 def rht(x, rht_seed=0):

@@ -120,6 +120,25 @@ int nvfp4_quantize_2d(const void* w, int dtype, int64_t rows, int64_t cols, int 
   return check_launch("nvfp4_quantize_2d");
 }
 
+int nvfp4_quantize_cast_transpose(const void* x, int dtype, int64_t rows, int64_t cols, int rounding,
+                                  uint64_t seed, uint64_t seed_t, int rht_t, uint64_t rht_seed, uint8_t* codes,
+                                  uint8_t* scales, float* tensor_scale, uint8_t* codes_t, uint8_t* scales_t,
+                                  float* tensor_scale_t, void* stream) {
+  if (!codes_t || !tensor_scale_t) return NVFP4_ERR_ARG;
+  int st = validate_quant(x, dtype, rows, cols, rounding, codes, scales, tensor_scale, codes_t, scales_t);
+  if (st) return st;
+  if (rht_t != 0 && rht_t != 1) return NVFP4_ERR_ARG;
+  if (rows % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!aligned(tensor_scale_t, 4)) return NVFP4_ERR_ALIGN;
+  int cus = 0;
+  if ((st = device_cus(&cus))) return st;
+  nvfp4::CastTransposeArgs a{x,      dtype == NVFP4_BF16, rows,   cols,         rounding, seed,     seed_t,
+                             rht_t == 1, rht_t ? nvfp4::rht_sign_mask(rht_seed) : 0u, codes, scales,
+                             tensor_scale, codes_t, scales_t, tensor_scale_t};
+  nvfp4::launch_cast_transpose(a, cus, (hipStream_t)stream);
+  return check_launch("nvfp4_quantize_cast_transpose");
+}
+
 int nvfp4_rht(const void* x, int dtype, int64_t rows, int64_t cols, uint64_t rht_seed, float* y,
               void* stream) {
   if (!x || !y) return NVFP4_ERR_ARG;

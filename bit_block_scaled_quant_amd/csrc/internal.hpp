@@ -25,6 +25,26 @@ struct QuantArgs {
 };
 
 void launch_quantize(const QuantArgs& a, int cus, hipStream_t st);
+
+// x [rows][cols] quantized rowwise (no transform) and columnwise (the rows
+// of x^T, with the transform when rht_t) in one pair of passes
+struct CastTransposeArgs {
+  const void* x;
+  bool bf16;
+  int64_t rows, cols;
+  int rounding;  // 0 RNE, 1 SR (both copies)
+  uint64_t seed, seed_t;
+  bool rht_t;
+  uint32_t rht_mask;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* tensor_scale;
+  uint8_t* codes_t;
+  uint8_t* scales_t;
+  float* tensor_scale_t;
+};
+
+void launch_cast_transpose(const CastTransposeArgs& a, int cus, hipStream_t st);
 void launch_rht(const void* x, bool bf16, int64_t rows, int64_t cols, uint32_t mask, float* y, int cus,
                 hipStream_t st);
 

@@ -83,11 +83,12 @@ __device__ __forceinline__ float div6(float t) {
 // decode and a division.
 constexpr int kInvTable = 128;
 
+__device__ __forceinline__ float inv_table_entry(uint32_t byte, float s_enc) {
+  return byte == 0 ? 0.0f : fminf(__fdiv_rn(s_enc, e4m3_decode(byte)), kFltMax);
+}
+
 __device__ __forceinline__ void build_inv_table(float* tab, float s_enc) {
-  if (threadIdx.x < kInvTable) {
-    const float sb = e4m3_decode(threadIdx.x);
-    tab[threadIdx.x] = threadIdx.x == 0 ? 0.0f : fminf(__fdiv_rn(s_enc, sb), kFltMax);
-  }
+  if (threadIdx.x < kInvTable) tab[threadIdx.x] = inv_table_entry(threadIdx.x, s_enc);
   __syncthreads();
 }
 
@@ -152,12 +153,10 @@ __device__ __forceinline__ uint32_t draw16(const Philox4& p, int j) {  // j in 0
 }
 
 // ------------------------------------------------------------- RHT -------
-// v <- 1/4 * H16 * diag(sigma) * v, in-place butterfly h = 1, 2, 4, 8, in
-// fp32; sign j flips when bit j of mask is set.
-__device__ __forceinline__ void rht16(float v[16], uint32_t mask) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((mask >> j) & 1u) << 31));
+// hadamard16: v <- H16 * v by the in-place butterfly h = 1, 2, 4, 8 in fp32,
+// then (QUARTER) the orthonormal 1/4.
+template <bool QUARTER = true>
+__device__ __forceinline__ void hadamard16(float v[16]) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -168,8 +167,19 @@ __device__ __forceinline__ void rht16(float v[16], uint32_t mask) {
       v[i + h] = a - b;
     }
   }
+  if (QUARTER) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = 0.25f * v[j];
+    for (int j = 0; j < 16; ++j) v[j] = 0.25f * v[j];
+  }
+}
+
+// rht16: v <- 1/4 * H16 * diag(sigma) * v; sign j flips when bit j of mask
+// is set.
+__device__ __forceinline__ void rht16(float v[16], uint32_t mask) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((mask >> j) & 1u) << 31));
+  hadamard16<true>(v);
 }
 
 // The same transform on a block held by a lane pair: the even lane holds

@@ -22,6 +22,9 @@
 //                   scale per block, each element encoded once and written
 //                   both ways, so the transposed copy is bit-identical to
 //                   quantizing W^T.
+// The cast-transpose (k_amax_ct, k_encode_ct) makes the rowwise copy and an
+// independently scaled columnwise copy (with the transform along columns)
+// from one read of x per pass.
 // k_rht writes the transform of 2B.2 alone (fp32 output).
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
@@ -597,6 +600,304 @@ __global__ __launch_bounds__(kThreads) void k_encode_2d(
   }
 }
 
+// ----------------------------------------------------- cast-transpose ----
+// Both operands a training step takes from one tensor x [R][C], read in its
+// own layout: the rowwise copy (1x16 blocks along rows, as nvfp4_quantize
+// makes it) and the columnwise copy (blocks of 16 rows of one column, i.e.
+// the rows of x^T, optionally through the transform of 2B.2 first) with a
+// tensor scale of its own.  x^T is never formed, and x is read once per
+// pass instead of once per copy and pass.
+//
+// A wave works on a chunk of 16 rows x 512 columns: lane l holds columns
+// 8l .. 8l + 7 of all 16 rows (one 16-byte load per row for bf16, two for
+// fp32), so a rowwise block sits in lanes 2k, 2k + 1 and a columnwise block
+// is one column of one lane.
+constexpr int kCtCols = 512;                 // columns of a chunk
+constexpr int kCtChunks = 8;                 // chunks per encode workgroup (a 128-row tile)
+constexpr int kCtThreads = 64 * kCtChunks;
+static_assert(kCtThreads == kCtCols, "the columnwise scale write-out takes one thread per column");
+
+template <bool BF16>
+struct Chunk16 {
+  uint4 w[16][BF16 ? 1 : 2];  // row j: the lane's eight columns
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_chunk(const void* __restrict__ x, int64_t e0, int64_t C,
+                                           Chunk16<BF16>& ch) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (BF16) {
+      ch.w[j][0] = ld_stream(static_cast<const uint16_t*>(x) + e0 + j * C);
+    } else {
+      const float* p = static_cast<const float*>(x) + e0 + j * C;
+      ch.w[j][0] = ld_stream(p);
+      ch.w[j][1] = ld_stream(p + 4);
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void zero_chunk(Chunk16<BF16>& ch) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int h = 0; h < (BF16 ? 1 : 2); ++h) ch.w[j][h] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The transform's sign flips on the raw storage: row j of a chunk is element
+// j of every columnwise block, so sign j flips all of row j.
+template <bool BF16>
+__device__ __forceinline__ void chunk_signs(Chunk16<BF16>& ch, uint32_t mask) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t f = ((mask >> j) & 1u) ? (BF16 ? 0x80008000u : 0x80000000u) : 0u;
+#pragma unroll
+    for (int h = 0; h < (BF16 ? 1 : 2); ++h) {
+      ch.w[j][h].x ^= f;
+      ch.w[j][h].y ^= f;
+      ch.w[j][h].z ^= f;
+      ch.w[j][h].w ^= f;
+    }
+  }
+}
+
+// element (row j, column k of the lane) as fp32; j and k are compile-time
+template <bool BF16>
+__device__ __forceinline__ float chunk_elem(const Chunk16<BF16>& ch, int j, int k) {
+  const uint4& q = ch.w[j][BF16 ? 0 : (k >> 2)];
+  const int wi = BF16 ? (k >> 1) : (k & 3);
+  const uint32_t w = wi == 0 ? q.x : wi == 1 ? q.y : wi == 2 ? q.z : q.w;
+  if (BF16) return __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  return __uint_as_float(w);
+}
+
+// max |v| as a tree (independent max3 chains rather than one serial chain)
+__device__ __forceinline__ float max_abs8(const float v[8]) {
+  const float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+  const float b = fmaxf(fmaxf(fabsf(v[3]), fabsf(v[4])), fabsf(v[5]));
+  return fmaxf(fmaxf(a, b), fmaxf(fabsf(v[6]), fabsf(v[7])));
+}
+
+__device__ __forceinline__ float max_abs16(const float v[16]) { return fmaxf(max_abs8(v), max_abs8(v + 8)); }
+
+// block_max_to for two maxima: m into ts[1], mt into ts_t[1]
+__device__ __forceinline__ void block_max2_to(float m, float mt, float* ts, float* ts_t) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    m = fmaxf(m, __shfl_xor(m, off));
+    mt = fmaxf(mt, __shfl_xor(mt, off));
+  }
+  __shared__ float red[2][kThreads / 64];
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = m;
+    red[1][threadIdx.x >> 6] = mt;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    float r = red[threadIdx.x][0];
+    for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[threadIdx.x][w]);
+    unsigned int* t = reinterpret_cast<unsigned int*>((threadIdx.x == 0 ? ts : ts_t) + 1);
+    const unsigned int bits = __float_as_uint(r);
+    if (bits > __hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(t, bits);
+  }
+}
+
+__global__ void k_init_amax2(float* ts, float* ts_t) {
+  ts[0] = 0.0f;
+  ts[1] = 0.0f;
+  ts_t[0] = 0.0f;
+  ts_t[1] = 0.0f;
+}
+
+// Pass 1 with the transform: the plain amax (rowwise copy) and the amax
+// after the transform of every 16-row column block (columnwise copy) from
+// one read.  |sigma x| = |x|, so the plain amax is taken after the flips.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_amax_ct(const void* __restrict__ x, int64_t R, int64_t C,
+                                                      uint32_t rht_mask, float* __restrict__ ts,
+                                                      float* __restrict__ ts_t) {
+  const int lane = threadIdx.x & 63;
+  const int64_t cchunks = (C + kCtCols - 1) / kCtCols;
+  const int64_t nchunks = (R / 16) * cchunks;
+  const int64_t wstride = (int64_t)gridDim.x * (kThreads / 64);
+  float m = 0.0f, mt = 0.0f;
+  for (int64_t q = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); q < nchunks; q += wstride) {
+    const int64_t col = (q % cchunks) * kCtCols + 8 * lane;
+    if (col >= C) continue;  // C % 16 == 0: a lane has all eight columns or none
+    Chunk16<BF16> ch;
+    load_chunk<BF16>(x, (q / cchunks) * 16 * C + col, C, ch);
+    chunk_signs<BF16>(ch, rht_mask);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = chunk_elem<BF16>(ch, j, k);
+      m = fmaxf(m, max_abs16(v));
+      hadamard16<false>(v);
+      mt = fmaxf(mt, max_abs16(v));
+    }
+  }
+  // the transform's final 1/4, applied to the maximum (rounding is monotone)
+  block_max2_to(m, 0.25f * mt, ts, ts_t);
+}
+
+// Pass 2.  A workgroup of eight waves takes a tile of 128 rows x 512 columns
+// (wave w: rows 16w .. 16w + 15).  Rowwise codes leave from registers, 256
+// contiguous bytes per store instruction; the columnwise codes (8 bytes per
+// column and chunk), the columnwise scales and the rowwise scales are
+// gathered in LDS and leave after one barrier as 16-byte pieces, four
+// threads per 64-byte column segment of x^T's codes.  Tiles are numbered
+// column-major and dealt to the eight XCDs in contiguous runs, so the two
+// tiles that complete one 128-byte line of x^T's codes (rows rt and
+// rt + 128) are neighbours in the same L2.
+// At most 128 VGPRs (four waves per SIMD: two workgroups per CU, whose load,
+// encode and write-out phases then overlap); unbounded, the compiler takes
+// about 170 and one workgroup per CU runs the phases back to back (measured
+// 30% slower).
+template <bool BF16, bool SR, bool RHT>
+__global__ __launch_bounds__(kCtThreads, 4) void k_encode_ct(
+    const void* __restrict__ x, int64_t R, int64_t C, uint64_t seed, uint64_t seed_t, uint32_t rht_mask,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts,
+    uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, float* __restrict__ ts_t) {
+  // columnwise codes [chunk][column slot][8 bytes]: lane l's eight columns
+  // fill bytes 64l .. 64l + 63 of a chunk row, column 8l + k in slot
+  // k ^ (l & 7) (the xor spreads a store instruction over the banks); 16
+  // bytes of padding per chunk row spread the write-out reads
+  constexpr int kPitch = kCtCols * 8 + 16;
+  __shared__ float inv_tab[2][kInvTable];
+  __shared__ __align__(16) uint8_t tq[kCtChunks * kPitch];
+  __shared__ __align__(16) uint8_t cs[kCtChunks][kCtCols];           // columnwise scales
+  __shared__ __align__(16) uint8_t rs[kCtChunks * 16][kCtCols / 16];  // rowwise scales
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const float amax = ts[1];
+  const float amax_t = RHT ? ts_t[1] : amax;
+  const float s_enc = tensor_scale_from_amax(amax), s_enc_t = tensor_scale_from_amax(amax_t);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ts[0] = s_enc;
+    ts_t[0] = s_enc_t;
+    if (!RHT) ts_t[1] = amax;
+  }
+  if (threadIdx.x < 2 * kInvTable)
+    inv_tab[threadIdx.x / kInvTable][threadIdx.x % kInvTable] =
+        inv_table_entry(threadIdx.x % kInvTable, threadIdx.x < kInvTable ? s_enc : s_enc_t);
+  __syncthreads();
+
+  const int64_t tiles_r = (R + 127) / 128, tiles_c = (C + kCtCols - 1) / kCtCols;
+  const int64_t ntiles = tiles_r * tiles_c, per_xcd = (ntiles + 7) / 8;
+  const int64_t tile = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (tile >= ntiles) return;  // the whole workgroup
+  const int64_t rt = (tile % tiles_r) * 128, c0 = (tile / tiles_r) * kCtCols;
+  const int nch = (int)min<int64_t>(kCtChunks, (R - rt) / 16);  // R % 16 == 0
+  const int ncols = (int)min<int64_t>(kCtCols, C - c0);         // C % 16 == 0
+  const int cl = 8 * lane;
+  const bool lane_ok = cl < ncols;  // the two lanes of a rowwise block agree
+  const int64_t r0 = rt + 16 * wv;
+
+  if (wv < nch) {  // wave-uniform: every lane of the wave takes part below
+    Chunk16<BF16> ch;
+    if (lane_ok)
+      load_chunk<BF16>(x, r0 * C + c0 + cl, C, ch);
+    else
+      zero_chunk<BF16>(ch);
+    const bool odd = lane & 1;
+    // rowwise copy: SR stream 0 of seed, element index r * C + c
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = chunk_elem<BF16>(ch, j, k);
+      float m = max_abs8(v);
+      m = fmaxf(m, lane_pair_swap(m));
+      float inv;
+      const uint32_t byte = block_scale(m, s_enc, inv_tab[0], &inv);
+      const int64_t e = (r0 + j) * C + c0 + cl;
+      const uint32_t q = encode8<SR>(v, inv, seed, 0u, (uint64_t)e);
+      if (lane_ok) *reinterpret_cast<uint32_t*>(codes + e / 2) = q;
+      if (!odd) rs[16 * wv + j][lane >> 1] = (uint8_t)byte;
+    }
+    // columnwise copy: the rows of x^T, SR stream 0 of seed_t, element index
+    // c * R + r (the index in x^T)
+    if (RHT) chunk_signs<BF16>(ch, rht_mask);
+    uint32_t sc_lo = 0u, sc_hi = 0u;
+    uint8_t* tqw = tq + wv * kPitch + 64 * lane;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = chunk_elem<BF16>(ch, j, k);
+      if (RHT) hadamard16<true>(v);
+      float inv;
+      const uint32_t byte = block_scale(max_abs16(v), s_enc_t, inv_tab[1], &inv);
+      const int64_t c = c0 + cl + k;
+      const uint2 q = encode16<SR>(v, inv, seed_t, 0u, (uint64_t)(c * R + r0));
+      *reinterpret_cast<uint2*>(tqw + 8 * (k ^ (lane & 7))) = q;
+      if (k < 4)
+        sc_lo |= byte << (8 * k);
+      else
+        sc_hi |= byte << (8 * (k - 4));
+    }
+    *reinterpret_cast<uint2*>(&cs[wv][cl]) = make_uint2(sc_lo, sc_hi);
+  }
+  __syncthreads();
+
+  // rowwise scales: 32 bytes per row of the tile
+  const int64_t srow = C / 16;
+  if (ncols == kCtCols && srow % 16 == 0 && ((uintptr_t)scales & 15) == 0) {
+    if (threadIdx.x < 32 * nch) {
+      const int row = threadIdx.x >> 1, p = threadIdx.x & 1;
+      *reinterpret_cast<uint4*>(scales + (rt + row) * srow + c0 / 16 + 16 * p) =
+          *reinterpret_cast<const uint4*>(&rs[row][16 * p]);
+    }
+  } else {
+    const int nb = ncols / 16;
+    for (int i = threadIdx.x; i < 16 * nch * nb; i += kCtThreads) {
+      const int row = i / nb, b = i % nb;
+      scales[(rt + row) * srow + c0 / 16 + b] = rs[row][b];
+    }
+  }
+  // columnwise codes: four threads per column, 16 bytes (two chunks) each
+  const int64_t tpitch = R / 2;
+  const bool t16 = tpitch % 16 == 0 && ((uintptr_t)codes_t & 15) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int item = threadIdx.x + kCtThreads * i;
+    const int cc = item >> 2, p = item & 3;
+    if (cc >= ncols || 2 * p >= nch) continue;
+    const int slot = 64 * (cc >> 3) + 8 * ((cc & 7) ^ ((cc >> 3) & 7));
+    const uint2 a = *reinterpret_cast<const uint2*>(tq + (2 * p) * kPitch + slot);
+    uint8_t* dst = codes_t + (c0 + cc) * tpitch + rt / 2 + 16 * p;
+    if (2 * p + 1 < nch) {
+      const uint2 b = *reinterpret_cast<const uint2*>(tq + (2 * p + 1) * kPitch + slot);
+      if (t16) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(a.x, a.y, b.x, b.y);
+      } else {
+        *reinterpret_cast<uint2*>(dst) = a;
+        *reinterpret_cast<uint2*>(dst + 8) = b;
+      }
+    } else {
+      *reinterpret_cast<uint2*>(dst) = a;
+    }
+  }
+  // columnwise scales: one thread per column, one byte per chunk
+  const int64_t spitch = R / 16;
+  if (threadIdx.x < ncols) {
+    const int cc = threadIdx.x;
+    uint8_t* dst = scales_t + (c0 + cc) * spitch + rt / 16;
+    if (nch == kCtChunks && spitch % 8 == 0 && ((uintptr_t)scales_t & 7) == 0) {
+      uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= (uint32_t)cs[i][cc] << (8 * i);
+        hi |= (uint32_t)cs[i + 4][cc] << (8 * i);
+      }
+      *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+    } else {
+      for (int i = 0; i < nch; ++i) dst[i] = cs[i][cc];
+    }
+  }
+}
+
 // ----------------------------------------------------------- RHT only ----
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_rht(const void* __restrict__ x, int64_t nchunks,
@@ -696,6 +997,48 @@ void launch_quantize(const QuantArgs& a, int cus, hipStream_t st) {
     launch_quantize_t<true>(a, cus, st);
   else
     launch_quantize_t<false>(a, cus, st);
+}
+
+template <bool BF16, bool SR, bool RHT>
+static void launch_ct_encode(const CastTransposeArgs& a, hipStream_t st) {
+  const int64_t tiles = ((a.rows + 127) / 128) * ((a.cols + kCtCols - 1) / kCtCols);
+  const int blocks = (int)(((tiles + 7) / 8) * 8);  // tiles <= 2^24 (rows * cols <= 2^40)
+  hipLaunchKernelGGL((k_encode_ct<BF16, SR, RHT>), dim3(blocks), dim3(kCtThreads), 0, st, a.x, a.rows, a.cols,
+                     a.seed, a.seed_t, a.rht_mask, a.codes, a.scales, a.tensor_scale, a.codes_t, a.scales_t,
+                     a.tensor_scale_t);
+}
+
+template <bool BF16>
+static void launch_cast_transpose_t(const CastTransposeArgs& a, int cus, hipStream_t st) {
+  const bool sr = a.rounding == 1;
+  if (a.rht_t) {
+    hipLaunchKernelGGL(k_init_amax2, dim3(1), dim3(1), 0, st, a.tensor_scale, a.tensor_scale_t);
+    const int64_t nchunks = (a.rows / 16) * ((a.cols + kCtCols - 1) / kCtCols);
+    const int blocks = (int)std::max<int64_t>(
+        1, std::min<int64_t>((nchunks + kThreads / 64 - 1) / (kThreads / 64), (int64_t)cus * 32));
+    hipLaunchKernelGGL(k_amax_ct<BF16>, dim3(blocks), dim3(kThreads), 0, st, a.x, a.rows, a.cols, a.rht_mask,
+                       a.tensor_scale, a.tensor_scale_t);
+    if (sr)
+      launch_ct_encode<BF16, true, true>(a, st);
+    else
+      launch_ct_encode<BF16, false, true>(a, st);
+  } else {
+    hipLaunchKernelGGL(k_init_amax, dim3(1), dim3(1), 0, st, a.tensor_scale);
+    const int64_t nvec = a.rows * a.cols / (BF16 ? 8 : 4);
+    hipLaunchKernelGGL((k_amax_plain<BF16>), dim3(grid_stride_blocks(nvec / 4, cus, 2)), dim3(kThreads), 0, st,
+                       reinterpret_cast<const uint4*>(a.x), nvec, a.tensor_scale);
+    if (sr)
+      launch_ct_encode<BF16, true, false>(a, st);
+    else
+      launch_ct_encode<BF16, false, false>(a, st);
+  }
+}
+
+void launch_cast_transpose(const CastTransposeArgs& a, int cus, hipStream_t st) {
+  if (a.bf16)
+    launch_cast_transpose_t<true>(a, cus, st);
+  else
+    launch_cast_transpose_t<false>(a, cus, st);
 }
 
 void launch_rht(const void* x, bool bf16, int64_t rows, int64_t cols, uint32_t mask, float* y, int cus,

@@ -105,6 +105,30 @@ int nvfp4_quantize_2d(const void* w, int dtype, int64_t rows, int64_t cols, int 
                       uint8_t* codes_t, uint8_t* scales_t, void* stream);
 
 /*
+ * Cast-transpose: the two NVFP4 copies of x [rows][cols] that a training
+ * step uses, made from x in its own layout (x^T is never formed; x is read
+ * once per pass instead of once per copy and pass).  2B.2 puts the Hadamard
+ * transform on the Wgrad inputs only, and Wgrad contracts over the rows of
+ * x, so the columnwise copy is the one that may take it:
+ *   codes [rows][cols/2], scales [rows][cols/16], tensor_scale[2]: exactly
+ *     nvfp4_quantize(x, dtype, rows, cols, rounding, seed, rht = 0);
+ *   codes_t [cols][rows/2], scales_t [cols][rows/16], tensor_scale_t[2]:
+ *     exactly nvfp4_quantize(x^T, dtype, cols, rows, rounding, seed_t,
+ *     rht_t, rht_seed), i.e. blocks of 16 consecutive rows of a column, with
+ *     their own amax (after the transform when rht_t = 1) and S_enc; SR draws
+ *     stream 0 of seed_t with element index c * rows + r.
+ * Pass a seed_t different from seed for draws independent of the rowwise
+ * copy's.  All six outputs are required.
+ * Shapes: rows >= 16, rows % 16 == 0, cols >= 16, cols % 16 == 0.
+ * Alignment: x 16 bytes; codes, codes_t 8 bytes; tensor scales 4 bytes.
+ */
+int nvfp4_quantize_cast_transpose(const void* x, int dtype, int64_t rows, int64_t cols, int rounding,
+                                  uint64_t seed, uint64_t seed_t, int rht_t, uint64_t rht_seed,
+                                  uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                  uint8_t* codes_t, uint8_t* scales_t, float* tensor_scale_t,
+                                  void* stream);
+
+/*
  * The random Hadamard transform of nvfp4_quantize (rht = 1) alone: y [rows]
  * [cols] fp32 = transform of every contiguous 16-chunk of every row of x.
  * nvfp4_quantize(x, rht = 1) equals nvfp4_quantize(y as f32, rht = 0) bit

@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_four_calls():
     names = declared_functions()
-    for n in ("nvfp4_quantize", "nvfp4_quantize_2d", "nvfp4_rht", "nvfp4_gemm",
-              "nvfp4_status_string", "nvfp4_last_error"):
+    for n in ("nvfp4_quantize", "nvfp4_quantize_2d", "nvfp4_quantize_cast_transpose", "nvfp4_rht",
+              "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error"):
         assert n in names
 
 
@@ -73,6 +73,27 @@ def test_quantize_2d_rejects_bad_arguments():
     assert f(A16, 3, 32, 64, 0, 0, A16, A16, A16, None, None, None) == -1
     assert f(A16, 1, 32, 64, 0, 0, A16, A16, A16, A16, None, None) == -1
     assert f(A8, 1, 32, 64, 0, 0, A16, A16, A16, None, None, None) == -3
+
+
+def test_cast_transpose_rejects_bad_arguments():
+    f = nv.lib().nvfp4_quantize_cast_transpose
+
+    def ct(x=A16, dtype=1, rows=32, cols=64, rounding=0, rht_t=1, codes=A16, scales=A16, ts=A16,
+           codes_t=A16, scales_t=A16, ts_t=A16):
+        return f(x, dtype, rows, cols, rounding, 0, 1, rht_t, 0, codes, scales, ts, codes_t, scales_t,
+                 ts_t, None)
+    assert ct(codes_t=None) == -1
+    assert ct(scales_t=None) == -1
+    assert ct(ts_t=None) == -1
+    assert ct(x=None) == -1
+    assert ct(rht_t=2) == -1
+    assert ct(rounding=3) == -1
+    assert ct(rows=40) == -2   # rows % 16
+    assert ct(cols=40) == -2   # cols % 16
+    assert ct(rows=0) == -2
+    assert ct(x=A8) == -3
+    assert ct(ts_t=ctypes.c_void_p(0x10002)) == -3
+    assert ct(codes_t=ctypes.c_void_p(0x10004)) == -3
 
 
 def test_rht_and_gemm_reject_bad_arguments():
