@@ -253,6 +253,27 @@ def main():
         for (name, _, _, _), (a, b) in zip(calls, ev):
             per_call[name].append(a.elapsed_time(b))
 
+    # outside the step: dequantization of dY's rowwise copy (HBM-bound)
+    extras = {}
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for dt, out_bytes, tag in ((torch.bfloat16, 2, "bf16"), (torch.float32, 4, "f32")):
+        out_t = torch.empty(TOKENS, FFN, dtype=dt, device=dev)
+
+        def deq():
+            nv.nvfp4_dequantize(qdY.codes, qdY.scales, qdY.tensor_scale, TOKENS, FFN, out_t)
+        deq()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(10):
+            deq()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / 10
+        gbs = TOKENS * FFN * (0.5 + 1.0 / 16.0 + out_bytes) / (ms * 1e-3) / 1e9
+        extras[f"dequantize_dY_{tag}"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
+                                          "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del out_t
+
     gemm_flops = 2.0 * TOKENS * FFN * HIDDEN
     step_flops = 3 * gemm_flops
     components = {}
@@ -307,6 +328,7 @@ def main():
         "quantize_frac_hbm_peak": round(quant_bytes_total / (quant_ms_total * 1e-3) / 1e9
                                         / HBM_PEAK_GBS, 4),
         "components": components,
+        "extras": extras,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -3,13 +3,13 @@
 A thin ctypes binding over ``libnvfp4.so`` (C ABI in ``include/nvfp4.h``).
 The functions named like the C entry points (``nvfp4_quantize``,
 ``nvfp4_quantize_2d``, ``nvfp4_quantize_cast_transpose``, ``nvfp4_rht``,
-``nvfp4_gemm``) only marshal torch
+``nvfp4_dequantize``, ``nvfp4_gemm``) only marshal torch
 tensors into pointers and the current HIP stream; every step of the
 computation runs in the library's HIP kernels.  There is no CPU fallback: if
 the library is missing, or a tensor is not on the GPU, the call raises.
 
 Convenience wrappers (``quantize``, ``quantize_2d``,
-``quantize_cast_transpose``, ``rht``, ``gemm``)
+``quantize_cast_transpose``, ``rht``, ``dequantize``, ``gemm``)
 allocate the outputs with torch (device memory only) and call the same
 entry points.
 """
@@ -58,6 +58,8 @@ def lib():
                                                     P]
         L.nvfp4_rht.restype = I
         L.nvfp4_rht.argtypes = [P, I, I64, I64, U64, P, P]
+        L.nvfp4_dequantize.restype = I
+        L.nvfp4_dequantize.argtypes = [P, P, P, I64, I64, I, P, P]
         L.nvfp4_gemm.restype = I
         L.nvfp4_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, P]
         L.nvfp4_status_string.restype = ctypes.c_char_p
@@ -128,6 +130,11 @@ def nvfp4_rht(x, rht_seed, y):
            "nvfp4_rht")
 
 
+def nvfp4_dequantize(codes, scales, tensor_scale, rows, cols, out):
+    _check(lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(tensor_scale), int(rows), int(cols),
+                                  _dtype(out), _ptr(out), _stream(out)), "nvfp4_dequantize")
+
+
 def nvfp4_gemm(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, M, N, K, c):
     _check(lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_codes),
                             _ptr(b_scales), _ptr(b_tensor_scale), int(M), int(N), int(K), _ptr(c),
@@ -195,6 +202,14 @@ def rht(x, rht_seed=0):
     y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     nvfp4_rht(x, rht_seed, y)
     return y
+
+
+def dequantize(q: Quantized, dtype=torch.float32):
+    """The values q encodes, rows x cols, as float32 or bfloat16."""
+    rows, cols = q.shape
+    out = torch.empty(rows, cols, dtype=dtype, device=q.codes.device)
+    nvfp4_dequantize(q.codes, q.scales, q.tensor_scale, rows, cols, out)
+    return out
 
 
 def gemm(a: Quantized, b: Quantized, out=None):

@@ -153,6 +153,20 @@ int nvfp4_rht(const void* x, int dtype, int64_t rows, int64_t cols, uint64_t rht
   return check_launch("nvfp4_rht");
 }
 
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t rows,
+                     int64_t cols, int out_dtype, void* out, void* stream) {
+  if (!codes || !scales || !tensor_scale || !out) return NVFP4_ERR_ARG;
+  if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_ERR_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0 || !size_ok(rows, cols)) return NVFP4_ERR_SHAPE;
+  if (!aligned(codes, 8) || !aligned(tensor_scale, 4) || !aligned(out, 16)) return NVFP4_ERR_ALIGN;
+  int cus = 0;
+  int st = device_cus(&cus);
+  if (st) return st;
+  nvfp4::launch_dequantize(codes, scales, tensor_scale, rows, cols, out_dtype == NVFP4_BF16, out, cus,
+                           (hipStream_t)stream);
+  return check_launch("nvfp4_dequantize");
+}
+
 int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale, int64_t M,
                int64_t N, int64_t K, float* c, void* stream) {

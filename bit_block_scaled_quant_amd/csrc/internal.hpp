@@ -47,6 +47,8 @@ struct CastTransposeArgs {
 void launch_cast_transpose(const CastTransposeArgs& a, int cus, hipStream_t st);
 void launch_rht(const void* x, bool bf16, int64_t rows, int64_t cols, uint32_t mask, float* y, int cus,
                 hipStream_t st);
+void launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t rows, int64_t cols,
+                       bool bf16_out, void* out, int cus, hipStream_t st);
 
 struct GemmArgs {
   const uint8_t* a_codes;

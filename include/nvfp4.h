@@ -138,6 +138,21 @@ int nvfp4_rht(const void* x, int dtype, int64_t rows, int64_t cols, uint64_t rht
               void* stream);
 
 /*
+ * Dequantization of an NVFP4 tensor of rows x cols (codes [rows][cols/2],
+ * scales [rows][cols/16], tensor_scale[0] = S_enc, read on the device):
+ * out[r][c] = e2m1(code) * e4m3(scale) / S_enc (2A: the block scale and the
+ * tensor scale undo the encoding's scaling).  The product is exact in fp32,
+ * so an fp32 output is the correctly rounded quotient; out_dtype NVFP4_BF16
+ * writes that fp32 value rounded to nearest-even bf16.  Scale bytes are those
+ * the quantizers produce (0x00 .. 0x7E).  Works for any copy, rowwise or
+ * transposed (a transposed copy dequantizes to x^T).
+ * Shapes: rows >= 1, cols >= 16, cols % 16 == 0.
+ * Alignment: codes 8 bytes, tensor_scale 4 bytes, out 16 bytes.
+ */
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                     int64_t rows, int64_t cols, int out_dtype, void* out, void* stream);
+
+/*
  * C [M][N] fp32 = deq(A) . deq(B)^T with FP32 accumulation, where A is an
  * NVFP4 tensor of M x K (codes [M][K/2], scales [M][K/16], tensor scale
  * a_tensor_scale[0]) and B one of N x K, both quantized along K.  Tensor

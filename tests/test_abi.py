@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("nvfp4_quantize", "nvfp4_quantize_2d", "nvfp4_quantize_cast_transpose", "nvfp4_rht",
-              "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error"):
+              "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error"):
         assert n in names
 
 
@@ -94,6 +94,16 @@ def test_cast_transpose_rejects_bad_arguments():
     assert ct(x=A8) == -3
     assert ct(ts_t=ctypes.c_void_p(0x10002)) == -3
     assert ct(codes_t=ctypes.c_void_p(0x10004)) == -3
+
+
+def test_dequantize_rejects_bad_arguments():
+    f = nv.lib().nvfp4_dequantize
+    assert f(None, A16, A16, 16, 32, 0, A16, None) == -1
+    assert f(A16, A16, A16, 16, 32, 2, A16, None) == -1   # out dtype
+    assert f(A16, A16, A16, 16, 24, 0, A16, None) == -2   # cols % 16
+    assert f(A16, A16, A16, 0, 32, 0, A16, None) == -2
+    assert f(A16, A16, A16, 16, 32, 0, A8, None) == -3    # out alignment
+    assert f(ctypes.c_void_p(0x10004), A16, A16, 16, 32, 0, A16, None) == -3
 
 
 def test_rht_and_gemm_reject_bad_arguments():
