@@ -1,4 +1,6 @@
-"""CPU reference ("the oracle") for the NVFP4 quantizer and block-scaled GEMM.
+"""CPU reference ("the oracle") for the NVFP4 quantizer and block-scaled GEMM
+(and for MXFP4, the 32-element power-of-two-scaled format they are compared
+against).
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU
 baseline leg of ``bench.py`` may use it; the product path never does.  The C
@@ -77,6 +79,14 @@ def lib():
         L.orc_sr_bits_n.argtypes = [U64, ctypes.c_uint32, U64, I64, P]
         L.orc_num_threads.restype = I
         L.orc_num_threads.argtypes = []
+        L.orc_mx_quantize.restype = I
+        L.orc_mx_quantize.argtypes = [P, I, I64, I64, P, P]
+        L.orc_e8m0_value.restype = ctypes.c_double
+        L.orc_e8m0_value.argtypes = [I]
+        L.orc_mx_dequantize.restype = I
+        L.orc_mx_dequantize.argtypes = [P, P, I64, I64, P]
+        L.orc_mx_gemm.restype = I
+        L.orc_mx_gemm.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P, P]
         _lib = L
     return _lib
 
@@ -262,3 +272,52 @@ def gemm_sample(a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, ii, jj):
 
 def num_threads():
     return lib().orc_num_threads()
+
+
+# --- MXFP4 ---------------------------------------------------------------
+def mx_quantize(x):
+    """Returns (codes [rows][cols/2], scales [rows][cols/32] E8M0 bytes)."""
+    x, dt = _input(x)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 32), dtype=np.uint8)
+    _check(lib().orc_mx_quantize(_ptr(x), dt, rows, cols, _ptr(codes), _ptr(scales)), "mx_quantize")
+    return codes, scales
+
+
+def e8m0_value(byte):
+    return lib().orc_e8m0_value(int(byte))
+
+
+def mx_dequantize(codes, scales):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((rows, cols), dtype=np.float64)
+    _check(lib().orc_mx_dequantize(_ptr(codes), _ptr(scales), rows, cols, _ptr(out)), "mx_dequantize")
+    return out
+
+
+def mx_gemm(a_codes, a_scales, b_codes, b_scales, ii=None, jj=None):
+    """C = deq(A) deq(B)^T in double (all of it, or at the (ii, jj) pairs),
+    and sum_k |a_ik b_jk| at the same positions."""
+    a_codes = np.ascontiguousarray(a_codes, dtype=np.uint8)
+    b_codes = np.ascontiguousarray(b_codes, dtype=np.uint8)
+    a_scales = np.ascontiguousarray(a_scales, dtype=np.uint8)
+    b_scales = np.ascontiguousarray(b_scales, dtype=np.uint8)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = b_codes.shape[0]
+    if ii is None:
+        count = M * N
+        c = np.empty((M, N), dtype=np.float64)
+        a = np.empty((M, N), dtype=np.float64)
+        pi = pj = None
+    else:
+        pi = np.ascontiguousarray(ii, dtype=np.int64)
+        pj = np.ascontiguousarray(jj, dtype=np.int64)
+        count = pi.size
+        c = np.empty(count, dtype=np.float64)
+        a = np.empty(count, dtype=np.float64)
+    _check(lib().orc_mx_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
+                             _ptr(pi), _ptr(pj), count, _ptr(c), _ptr(a)), "mx_gemm")
+    return c, a

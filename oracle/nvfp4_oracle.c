@@ -530,3 +530,101 @@ int orc_gemm_sample(const uint8_t* a_codes, const uint8_t* a_scales, float a_s_e
     dot(a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, K, ii[t], jj[t], &c[t], &abs_sum[t]);
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 (the format the pages compare NVFP4 against)                  */
+/* ------------------------------------------------------------------ */
+
+/* [MX] E8M0 scale exponent of a 32-element block: floor(log2(amax)) - 2,
+ * where 2 is the exponent of E2M1's largest normal (6 = 1.5 * 2^2), clamped
+ * to the E8M0 range [-127, 127]; an all-zero block takes -127 (byte 0). */
+static int mx_scale_exponent(float amax) {
+  if (amax == 0.0f) return -127;
+  int e;
+  frexp((double)amax, &e); /* amax = f * 2^e with f in [0.5, 1): floor(log2) = e - 1 */
+  int s = (e - 1) - 2;
+  if (s < -127) s = -127;
+  if (s > 127) s = 127;
+  return s;
+}
+
+/* [MX] 1D MXFP4 along cols: each block of 32 consecutive elements of a row
+ * gets the E8M0 byte s + 127 and each element the E2M1 code of V / 2^s by R4
+ * (nearest, ties to the even code, saturating at 6, sign kept).  V / 2^s is
+ * formed exactly in double; narrowing it to float changes only values below
+ * 2^-126, which encode to a signed zero either way. */
+int orc_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                    uint8_t* scales) {
+  if (!x || !codes || !scales) return ORC_E_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_E_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 32) return ORC_E_SHAPE;
+  int st = check_input(x, dtype, rows * cols);
+  if (st) return st;
+#pragma omp parallel for
+  for (int64_t r = 0; r < rows; ++r) {
+    uint8_t* crow = codes + r * (cols / 2);
+    for (int64_t b = 0; b < cols / 32; ++b) {
+      float amax = 0.0f;
+      for (int k = 0; k < 32; ++k) {
+        const float a = fabsf(load_elem(x, dtype, r * cols + 32 * b + k));
+        if (a > amax) amax = a;
+      }
+      const int s = mx_scale_exponent(amax);
+      scales[r * (cols / 32) + b] = (uint8_t)(s + 127);
+      for (int k = 0; k < 32; ++k) {
+        const double y = ldexp((double)load_elem(x, dtype, r * cols + 32 * b + k), -s);
+        put_code(crow, 32 * b + k, orc_e2m1_encode_rne((float)y));
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* [MX] value of an E8M0 byte: 2^(byte - 127); 0xFF is NaN */
+double orc_e8m0_value(int byte) {
+  if ((byte & 0xFF) == 0xFF) return NAN;
+  return ldexp(1.0, (byte & 0xFF) - 127);
+}
+
+static double mx_deq(const uint8_t* codes, const uint8_t* scales, int64_t K, int64_t i, int64_t k) {
+  const uint8_t byte = codes[i * (K / 2) + k / 2];
+  const int code = (k & 1) ? (byte >> 4) : (byte & 0x0F);
+  return orc_e2m1_value(code) * orc_e8m0_value(scales[i * (K / 32) + k / 32]);
+}
+
+/* out[r][c] = e2m1(code) * 2^(scale - 127), in double */
+int orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                      double* out) {
+  if (!codes || !scales || !out) return ORC_E_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 32) return ORC_E_SHAPE;
+#pragma omp parallel for
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) out[r * cols + c] = mx_deq(codes, scales, cols, r, c);
+  return ORC_OK;
+}
+
+/* [ACC] C_ij = sum_k deq(A)_ik * deq(B)_jk in double, for the (ii, jj) pairs
+ * given (or every pair when ii == NULL: count must be M * N, row-major). */
+int orc_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, const int64_t* ii,
+                const int64_t* jj, int64_t count, double* c, double* abs_sum) {
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !c || !abs_sum) return ORC_E_ARG;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 32) return ORC_E_SHAPE;
+  if (!ii != !jj) return ORC_E_ARG;
+  if (!ii && count != M * N) return ORC_E_ARG;
+  for (int64_t t = 0; ii && t < count; ++t)
+    if (ii[t] < 0 || ii[t] >= M || jj[t] < 0 || jj[t] >= N) return ORC_E_ARG;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < count; ++t) {
+    const int64_t i = ii ? ii[t] : t / N, j = jj ? jj[t] : t % N;
+    double acc = 0.0, acc_abs = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double p = mx_deq(a_codes, a_scales, K, i, k) * mx_deq(b_codes, b_scales, K, j, k);
+      acc += p;
+      acc_abs += fabs(p);
+    }
+    c[t] = acc;
+    abs_sum[t] = acc_abs;
+  }
+  return ORC_OK;
+}

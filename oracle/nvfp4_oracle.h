@@ -31,6 +31,12 @@
  *            0x7F/0xFF NaN.
  *   [PHILOX] Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
  *            1, 2, 3", SC'11: Philox4x32 with 10 rounds.
+ *   [MX]     OCP Microscaling Formats (MX) v1.0, section 6.3 (conversion of a
+ *            vector to an MX block): MXFP4 = 32-element blocks of E2M1 with an
+ *            E8M0 (power-of-two) scale 2^(floor(log2(amax)) - emax_elem), the
+ *            format "Pretraining Large Language Models with NVFP4",
+ *            Technische samenvatting 2A, compares NVFP4 against (32 vs 16
+ *            elements, UE8M0 vs E4M3 scales).
  *
  * Parity status: every function here is pinned by tests/test_oracle_*.py
  * (closed forms, exhaustive codec checks, invariants, library routines,
@@ -114,6 +120,19 @@ int orc_gemm_sample(const uint8_t* a_codes, const uint8_t* a_scales, float a_s_e
                     double* c, double* abs_sum);
 
 int orc_num_threads(void);
+
+/* --- MXFP4 ([MX]) ---------------------------------------------------- */
+/* 1D along cols (cols % 32 == 0): codes [rows][cols/2] (two per byte, even
+ * element low), scales [rows][cols/32] E8M0 bytes; round-to-nearest-even. */
+int orc_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                    uint8_t* scales);
+double orc_e8m0_value(int byte);
+int orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                      double* out);
+/* C_ij in double for the given (ii[t], jj[t]) pairs, or all M*N (ii = jj = NULL) */
+int orc_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, const int64_t* ii,
+                const int64_t* jj, int64_t count, double* c, double* abs_sum);
 
 #ifdef __cplusplus
 }
