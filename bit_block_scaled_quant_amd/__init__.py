@@ -3,13 +3,15 @@
 A thin ctypes binding over ``libnvfp4.so`` (C ABI in ``include/nvfp4.h``).
 The functions named like the C entry points (``nvfp4_quantize``,
 ``nvfp4_quantize_2d``, ``nvfp4_quantize_cast_transpose``, ``nvfp4_rht``,
-``nvfp4_dequantize``, ``nvfp4_gemm``) only marshal torch
+``nvfp4_dequantize``, ``nvfp4_gemm``, and ``mxfp4_quantize``,
+``mxfp4_dequantize``, ``mxfp4_gemm``) only marshal torch
 tensors into pointers and the current HIP stream; every step of the
 computation runs in the library's HIP kernels.  There is no CPU fallback: if
 the library is missing, or a tensor is not on the GPU, the call raises.
 
 Convenience wrappers (``quantize``, ``quantize_2d``,
-``quantize_cast_transpose``, ``rht``, ``dequantize``, ``gemm``)
+``quantize_cast_transpose``, ``rht``, ``dequantize``, ``gemm``, ``mx_quantize``,
+``mx_dequantize``, ``mx_gemm``)
 allocate the outputs with torch (device memory only) and call the same
 entry points.
 """
@@ -62,6 +64,12 @@ def lib():
         L.nvfp4_dequantize.argtypes = [P, P, P, I64, I64, I, P, P]
         L.nvfp4_gemm.restype = I
         L.nvfp4_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, P]
+        L.mxfp4_quantize.restype = I
+        L.mxfp4_quantize.argtypes = [P, I, I64, I64, P, P, P]
+        L.mxfp4_dequantize.restype = I
+        L.mxfp4_dequantize.argtypes = [P, P, I64, I64, I, P, P]
+        L.mxfp4_gemm.restype = I
+        L.mxfp4_gemm.argtypes = [P, P, P, P, I64, I64, I64, P, P]
         L.nvfp4_status_string.restype = ctypes.c_char_p
         L.nvfp4_status_string.argtypes = [I]
         L.nvfp4_last_error.restype = ctypes.c_char_p
@@ -139,6 +147,22 @@ def nvfp4_gemm(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_sc
     _check(lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_codes),
                             _ptr(b_scales), _ptr(b_tensor_scale), int(M), int(N), int(K), _ptr(c),
                             _stream(c)), "nvfp4_gemm")
+
+
+def mxfp4_quantize(x, codes, scales):
+    rows, cols = x.shape
+    _check(lib().mxfp4_quantize(_ptr(x), _dtype(x), rows, cols, _ptr(codes), _ptr(scales), _stream(x)),
+           "mxfp4_quantize")
+
+
+def mxfp4_dequantize(codes, scales, rows, cols, out):
+    _check(lib().mxfp4_dequantize(_ptr(codes), _ptr(scales), int(rows), int(cols), _dtype(out), _ptr(out),
+                                  _stream(out)), "mxfp4_dequantize")
+
+
+def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, c):
+    _check(lib().mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), int(M), int(N),
+                            int(K), _ptr(c), _stream(c)), "mxfp4_gemm")
 
 
 # ---- convenience wrappers ---------------------------------------------------
@@ -220,4 +244,41 @@ def gemm(a: Quantized, b: Quantized, out=None):
         raise ValueError(f"K mismatch: {K} vs {K2}")
     c = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=a.codes.device)
     nvfp4_gemm(a.codes, a.scales, a.tensor_scale, b.codes, b.scales, b.tensor_scale, M, N, K, c)
+    return c
+
+
+@dataclass
+class MxQuantized:
+    """An MXFP4 tensor of rows x cols quantized along cols."""
+    codes: torch.Tensor   # uint8 [rows][cols/2]
+    scales: torch.Tensor  # uint8 [rows][cols/32], E8M0
+
+    @property
+    def shape(self):
+        return (self.codes.shape[0], self.codes.shape[1] * 2)
+
+
+def mx_quantize(x) -> MxQuantized:
+    rows, cols = x.shape
+    q = MxQuantized(torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device),
+                    torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device))
+    mxfp4_quantize(x, q.codes, q.scales)
+    return q
+
+
+def mx_dequantize(q: MxQuantized, dtype=torch.float32):
+    rows, cols = q.shape
+    out = torch.empty(rows, cols, dtype=dtype, device=q.codes.device)
+    mxfp4_dequantize(q.codes, q.scales, rows, cols, out)
+    return out
+
+
+def mx_gemm(a: MxQuantized, b: MxQuantized, out=None):
+    """C = deq(a) . deq(b)^T, fp32 [M][N]."""
+    M, K = a.shape
+    N, K2 = b.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: {K} vs {K2}")
+    c = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=a.codes.device)
+    mxfp4_gemm(a.codes, a.scales, b.codes, b.scales, M, N, K, c)
     return c

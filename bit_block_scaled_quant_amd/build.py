@@ -4,7 +4,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC_DIR = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "quantize.hip", "dequantize.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "dequantize.hip", "gemm.hip", "mx.hip"]
 LIB_PATH = os.path.join(HERE, "libnvfp4.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -167,6 +167,44 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
   return check_launch("nvfp4_dequantize");
 }
 
+int mxfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                   void* stream) {
+  if (!x || !codes || !scales) return NVFP4_ERR_ARG;
+  if (dtype != NVFP4_F32 && dtype != NVFP4_BF16) return NVFP4_ERR_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 32 != 0 || !size_ok(rows, cols)) return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(codes, 8)) return NVFP4_ERR_ALIGN;
+  int cus = 0;
+  int st = device_cus(&cus);
+  if (st) return st;
+  nvfp4::launch_mx_quantize(x, dtype == NVFP4_BF16, rows, cols, codes, scales, cus, (hipStream_t)stream);
+  return check_launch("mxfp4_quantize");
+}
+
+int mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, int out_dtype,
+                     void* out, void* stream) {
+  if (!codes || !scales || !out) return NVFP4_ERR_ARG;
+  if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_ERR_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 32 != 0 || !size_ok(rows, cols)) return NVFP4_ERR_SHAPE;
+  if (!aligned(codes, 8) || !aligned(out, 16)) return NVFP4_ERR_ALIGN;
+  int cus = 0;
+  int st = device_cus(&cus);
+  if (st) return st;
+  nvfp4::launch_mx_dequantize(codes, scales, rows, cols, out_dtype == NVFP4_BF16, out, cus, (hipStream_t)stream);
+  return check_launch("mxfp4_dequantize");
+}
+
+int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+               int64_t M, int64_t N, int64_t K, float* c, void* stream) {
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return NVFP4_ERR_ARG;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (!size_ok(M, K) || !size_ok(N, K) || !size_ok(M, N)) return NVFP4_ERR_SHAPE;
+  if (M > INT64_C(65535) * 64) return NVFP4_ERR_SHAPE;  // grid.y of the general path
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(c, 4)) return NVFP4_ERR_ALIGN;
+  nvfp4::MxGemmArgs g{a_codes, a_scales, b_codes, b_scales, M, N, K, c};
+  nvfp4::launch_mx_gemm(g, (hipStream_t)stream);
+  return check_launch("mxfp4_gemm");
+}
+
 int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale, int64_t M,
                int64_t N, int64_t K, float* c, void* stream) {

@@ -21,18 +21,6 @@ namespace nvfp4 {
 constexpr int kDqThreads = 256;
 constexpr int kDqTable = 128 * 8;  // [scale byte & 0x7F][code magnitude]
 
-__device__ __forceinline__ float e2m1_magnitude(uint32_t m) {  // m in 0..7
-  // 0, 0.5, 1, 1.5, 2, 3, 4, 6
-  const float sub = 0.5f * (float)m;                                          // m < 4
-  const float nrm = __uint_as_float(((m >> 1) + 126u) << 23 | (m & 1u) << 22);  // 2^(m/2 - 1) * (1 + (m & 1) / 2)
-  return m < 4 ? sub : nrm;
-}
-
-__device__ __forceinline__ uint32_t bf16_rne(float v) {  // finite or inf
-  const uint32_t b = __float_as_uint(v);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
 template <bool BF16OUT>
 __global__ __launch_bounds__(kDqThreads) void k_dequantize(const uint8_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ scales,

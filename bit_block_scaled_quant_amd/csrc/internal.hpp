@@ -63,4 +63,20 @@ struct GemmArgs {
 
 void launch_gemm(const GemmArgs& g, int cus, hipStream_t st);
 
+// MXFP4: 32-element blocks of E2M1 codes with E8M0 (power-of-two) scales
+struct MxGemmArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  int64_t M, N, K;
+  float* c;
+};
+
+void launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                        int cus, hipStream_t st);
+void launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, bool bf16_out,
+                          void* out, int cus, hipStream_t st);
+void launch_mx_gemm(const MxGemmArgs& g, hipStream_t st);
+
 }  // namespace nvfp4

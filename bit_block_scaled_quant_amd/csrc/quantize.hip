@@ -35,42 +35,6 @@ constexpr int kThreads = 256;
 static_assert(kThreads >= kInvTable, "the inverse-scale table is built by one thread per entry");
 constexpr int kTile = 128;
 
-// raw storage of eight consecutive input elements (e % 8 == 0)
-template <bool BF16>
-struct Raw8 {
-  uint4 a, b;  // b unused for bf16
-};
-
-template <bool BF16>
-__device__ __forceinline__ Raw8<BF16> load8_raw(const void* __restrict__ x, int64_t e) {
-  Raw8<BF16> r;
-  if (BF16) {
-    r.a = ld_stream(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e));
-    r.b = make_uint4(0u, 0u, 0u, 0u);
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + e);
-    r.a = ld_stream(p);
-    r.b = ld_stream(p + 1);
-  }
-  return r;
-}
-
-template <bool BF16>
-__device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float v[8]) {
-  if (BF16) {
-    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-    v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y); v[2] = __uint_as_float(r.a.z);
-    v[3] = __uint_as_float(r.a.w); v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
-    v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
-  }
-}
-
 // codes of eight elements (element index0 .. index0 + 7, index0 % 8 == 0)
 template <bool SR>
 __device__ __forceinline__ uint32_t encode8(const float v[8], float inv, uint64_t seed, uint32_t stream,
@@ -671,15 +635,6 @@ __device__ __forceinline__ float chunk_elem(const Chunk16<BF16>& ch, int j, int 
   if (BF16) return __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
   return __uint_as_float(w);
 }
-
-// max |v| as a tree (independent max3 chains rather than one serial chain)
-__device__ __forceinline__ float max_abs8(const float v[8]) {
-  const float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
-  const float b = fmaxf(fmaxf(fabsf(v[3]), fabsf(v[4])), fabsf(v[5]));
-  return fmaxf(fmaxf(a, b), fmaxf(fabsf(v[6]), fabsf(v[7])));
-}
-
-__device__ __forceinline__ float max_abs16(const float v[16]) { return fmaxf(max_abs8(v), max_abs8(v + 8)); }
 
 // block_max_to for two maxima: m into ts[1], mt into ts_t[1]
 __device__ __forceinline__ void block_max2_to(float m, float mt, float* ts, float* ts_t) {

@@ -166,6 +166,40 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_t
                const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale,
                int64_t M, int64_t N, int64_t K, float* c, void* stream);
 
+/*
+ * MXFP4, the format the NVFP4 recipe is measured against (2A: blocks of 32
+ * elements with a UE8M0 scale instead of 16 with E4M3, and no per-tensor
+ * scale).  Conversion as OCP Microscaling Formats (MX) v1.0, section 6.3:
+ * a block of 32 consecutive elements of a row with absolute maximum amax
+ * shares X = 2^(floor(log2 amax) - 2), stored as the E8M0 byte
+ * log2(X) + 127 clamped to >= 0 (0 for an all-zero block); each element is
+ * x / X rounded to E2M1, nearest-even, saturating at 6, sign kept.
+ *   codes [rows][cols/2] (element 2k in the low nibble), scales [rows][cols/32].
+ * Shapes: rows >= 1, cols >= 32, cols % 32 == 0.  Alignment: x 16, codes 8.
+ */
+int mxfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                   uint8_t* scales, void* stream);
+
+/*
+ * out [rows][cols] = e2m1(code) * 2^(scale - 127), exact in fp32; bf16 output
+ * (out_dtype NVFP4_BF16) is that value rounded to nearest-even.  Shapes as
+ * mxfp4_quantize.  Alignment: codes 8 bytes, out 16 bytes.
+ */
+int mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                     int out_dtype, void* out, void* stream);
+
+/*
+ * C [M][N] fp32 = deq(A) . deq(B)^T for MXFP4 A [M x K] and B [N x K], both
+ * quantized along K, with FP32 accumulation on gfx950's scaled FP4 matrix
+ * instruction (products of E2M1 values and power-of-two scales are exact).
+ * Any result within 1e-5 * sum_k |deq(A)_ik deq(B)_jk| of the exact sum is
+ * correct.  Shapes: M, N >= 1, K >= 32, K % 32 == 0 (M, N and K multiples
+ * of 256 with 8-byte aligned scales take the fast path).
+ * Alignment: codes 16 bytes, C 4 bytes.
+ */
+int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+               const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* c, void* stream);
+
 /* Static text for a status code. */
 const char* nvfp4_status_string(int status);
 /* Text of the last NVFP4_ERR_HIP on the calling thread ("" if none). */

@@ -17,13 +17,14 @@ HEADER = os.path.join(ROOT, "include", "nvfp4.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:nv|mx)fp4_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("nvfp4_quantize", "nvfp4_quantize_2d", "nvfp4_quantize_cast_transpose", "nvfp4_rht",
-              "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error"):
+              "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error",
+              "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm"):
         assert n in names
 
 
@@ -104,6 +105,21 @@ def test_dequantize_rejects_bad_arguments():
     assert f(A16, A16, A16, 0, 32, 0, A16, None) == -2
     assert f(A16, A16, A16, 16, 32, 0, A8, None) == -3    # out alignment
     assert f(ctypes.c_void_p(0x10004), A16, A16, 16, 32, 0, A16, None) == -3
+
+
+def test_mx_calls_reject_bad_arguments():
+    L = nv.lib()
+    assert L.mxfp4_quantize(A16, 1, 4, 48, A16, A16, None) == -2   # cols % 32
+    assert L.mxfp4_quantize(A16, 2, 4, 64, A16, A16, None) == -1
+    assert L.mxfp4_quantize(None, 1, 4, 64, A16, A16, None) == -1
+    assert L.mxfp4_quantize(A8, 1, 4, 64, A16, A16, None) == -3
+    assert L.mxfp4_dequantize(A16, A16, 4, 48, 0, A16, None) == -2
+    assert L.mxfp4_dequantize(A16, A16, 4, 64, 0, A8, None) == -3
+    g = L.mxfp4_gemm
+    assert g(A16, A16, A16, A16, 16, 16, 48, A16, None) == -2   # K % 32
+    assert g(A16, A16, A16, A16, 0, 16, 64, A16, None) == -2
+    assert g(None, A16, A16, A16, 16, 16, 64, A16, None) == -1
+    assert g(A8, A16, A16, A16, 16, 16, 64, A16, None) == -3    # codes 16-byte aligned
 
 
 def test_rht_and_gemm_reject_bad_arguments():
