@@ -274,6 +274,55 @@ def main():
                                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         del out_t
 
+    # MXFP4, the format the pages measure NVFP4 against: the same three GEMMs
+    # on gfx950's scaled FP4 MFMA, its quantizer, and the quantization error
+    # of both formats on the layer's tensors (a dataset-free proxy for the
+    # pages' accuracy comparison).  Outside the step.
+    def timed_ms(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    Wt = W.t().contiguous()
+    dYt_m = dY.t().contiguous()
+    Xt_m = X.t().contiguous()
+    mx_ops = {"fprop": (X, W), "dgrad": (dY, Wt), "wgrad": (dYt_m, Xt_m)}
+    mxq = {}
+    for name, (a, b) in mx_ops.items():
+        qa, qb = nv.mx_quantize(a), nv.mx_quantize(b)
+        M, K = a.shape
+        N = b.shape[0]
+        cbuf = {"fprop": Y, "dgrad": dX, "wgrad": dW}[name]
+        ms = timed_ms(lambda: nv.mx_gemm(qa, qb, out=cbuf))
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        extras[f"mxfp4_gemm_{name}"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                                        "frac_fp4_mfma_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
+        mxq[name] = (qa, M, K)
+    qa, M, K = mxq["dgrad"]
+    ms = timed_ms(lambda: nv.mxfp4_quantize(dY, qa.codes, qa.scales))
+    gbs = M * K * (2 + 0.5 + 1.0 / 32.0) / (ms * 1e-3) / 1e9
+    extras["mxfp4_quantize_dY"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
+                                   "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del Wt, dYt_m, Xt_m, mxq, qa
+
+    def rel_err(t, deq):
+        d = (deq.double() - t.double())
+        return float(torch.linalg.vector_norm(d) / torch.linalg.vector_norm(t.double()))
+
+    err = {}
+    for name, t, two_d in (("X", X, False), ("W", W, True), ("dY", dY, False)):
+        qn = nv.quantize_2d(t, transposed=False) if two_d else nv.quantize(t)
+        e_nv = rel_err(t, nv.dequantize(qn))
+        del qn
+        e_mx = rel_err(t, nv.mx_dequantize(nv.mx_quantize(t)))
+        err[name] = {"nvfp4": round(e_nv, 5), "mxfp4": round(e_mx, 5)}
+    extras["relative_rms_quantization_error"] = err
+
     gemm_flops = 2.0 * TOKENS * FFN * HIDDEN
     step_flops = 3 * gemm_flops
     components = {}

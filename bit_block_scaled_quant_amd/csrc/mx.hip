@@ -130,8 +130,9 @@ __device__ __forceinline__ floatx16 mx_mfma(const uint4& a, const uint4& b, floa
   }
 }
 
-// Fast path: M, N multiples of 256, K a multiple of 256, 16-byte aligned
-// codes, 8-byte aligned scales.  A 256-thread workgroup owns a 256 x 256
+// Fast path: M, N multiples of 256, K a multiple of 256 (at most 2^24, so
+// a tile's byte offsets fit in 32 bits), 16-byte aligned codes, 8-byte
+// aligned scales.  A 256-thread workgroup owns a 256 x 256
 // tile of C; its four waves (2 x 2) own 128 x 128 each as 4 x 4 MFMA tiles
 // (256 accumulators per lane).  K advances in stages of 256 elements: 128
 // code bytes per row of A and B (32 KB each) and 8 scale bytes per row
@@ -162,7 +163,7 @@ __device__ __forceinline__ void mx_issue(const MxGemmArgs& g, int64_t m0, int64_
     const int blk = 8 * wave + u;
     const int row = 8 * blk + (lane >> 3);
     const int chunk = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
-    const int64_t off = row * kb + 16 * chunk;
+    const uint32_t off = (uint32_t)(row * kb + 16 * chunk);  // < 2^31 (K <= 2^24)
     __builtin_amdgcn_global_load_lds((mx_glb_void_t*)(a0 + off), (mx_lds_void_t*)(buf + 1024 * blk), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((mx_glb_void_t*)(b0 + off), (mx_lds_void_t*)(buf + kMxOffB + 1024 * blk),
                                      16, 0, 0);
@@ -173,7 +174,7 @@ __device__ __forceinline__ void mx_issue(const MxGemmArgs& g, int64_t m0, int64_
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int slot = 256 * u + 64 * wave + lane;
-    const int64_t off = (slot >> 1) * ks + 4 * (slot & 1);
+    const uint32_t off = (uint32_t)((slot >> 1) * ks + 4 * (slot & 1));
     __builtin_amdgcn_global_load_lds((mx_glb_void_t*)(as0 + off),
                                      (mx_lds_void_t*)(buf + kMxOffAS + 1024 * u + 256 * wave), 4, 0, 0);
     __builtin_amdgcn_global_load_lds((mx_glb_void_t*)(bs0 + off),
@@ -201,23 +202,76 @@ __device__ __forceinline__ uint32_t mx_scales(const uint8_t* base, int row, uint
   return __builtin_amdgcn_perm(s.y, s.x, sel);
 }
 
-__device__ __forceinline__ void mx_stage(const uint8_t* cur, int wm, int wn, int r, int g, MxFrag& f,
+__device__ __forceinline__ void mx_read_scales(const uint8_t* buf, int wm, int wn, int r, uint32_t sel,
+                                               uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sa[i] = mx_scales(buf + kMxOffAS, wm * 128 + i * 32 + r, sel);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sb[j] = mx_scales(buf + kMxOffBS, wn * 128 + j * 32 + r, sel);
+}
+
+template <int T>
+__device__ __forceinline__ void mx_mfmas(const MxFrag& f, const uint32_t (&sa)[4], const uint32_t (&sb)[4],
                                          floatx16 (&acc)[4][4]) {
-  const uint32_t sel = g ? 0x07050301u : 0x06040200u;
-  uint32_t sa[4], sb[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sa[i] = mx_scales(cur + kMxOffAS, wm * 128 + i * 32 + r, sel);
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sb[j] = mx_scales(cur + kMxOffBS, wn * 128 + j * 32 + r, sel);
+    for (int j = 0; j < 4; ++j) acc[i][j] = mx_mfma(f.a[i], f.b[j], acc[i][j], sa[i], sb[j], T);
+}
+
+// Instruction order of one step: the 16 MFMAs, with READS LDS reads (the
+// next step's fragments, and at a stage's end the next stage's scales) and
+// VALU VALU ops placed one after each of the first MFMAs, so that the matrix
+// core stays busy while the reads are in flight (left alone, the compiler
+// issues a whole stage of reads, waits, then all 64 MFMAs).
+template <int READS, int VALU>
+__device__ __forceinline__ void mx_order() {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    MxFrag fn;
-    if (t < 3) mx_read(cur, wm, wn, r, g, t + 1, fn);  // next step's fragments under these MFMAs
+  for (int k = 0; k < 16; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (k < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (k >= 16 - VALU) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+  }
+}
+
+// One stage from cur.  In: f = step 0 of cur, sa/sb = cur's scales.  Out: the
+// same for nxt.  The barrier sits before the last step: by then every wave
+// has read all of cur into registers and its loads of nxt have landed; the
+// stage after nxt then streams into cur while the last step's MFMAs cover
+// the reads of nxt's first step.
+__device__ __forceinline__ void mx_stage(const MxGemmArgs& g, int64_t m0, int64_t n0, bool issue, int64_t k_issue,
+                                         uint8_t* cur, const uint8_t* nxt, MxFrag& f, uint32_t (&sa)[4],
+                                         uint32_t (&sb)[4], floatx16 (&acc)[4][4], int wm, int wn, int r, int gq,
+                                         uint32_t sel) {
+  MxFrag fn;
+  mx_mfmas<0>(f, sa, sb, acc);
+  mx_read(cur, wm, wn, r, gq, 1, fn);
+  mx_order<8, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  mx_mfmas<1>(fn, sa, sb, acc);
+  mx_read(cur, wm, wn, r, gq, 2, f);
+  mx_order<8, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  mx_mfmas<2>(f, sa, sb, acc);
+  mx_read(cur, wm, wn, r, gq, 3, fn);
+  mx_order<8, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // waits for this wave's loads of nxt (vmcnt(0)), then every wave
+  // Unconditional, so the stage has no branch (with one, the compiler sinks
+  // the MFMAs below it and issues the stage's reads first): past the last
+  // stage it reloads stage 0 into a buffer no one reads again.
+  mx_issue(g, m0, n0, issue ? k_issue : 0, cur);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t na[4], nb[4];
+  mx_mfmas<3>(fn, sa, sb, acc);
+  mx_read(nxt, wm, wn, r, gq, 0, f);
+  mx_read_scales(nxt, wm, wn, r, sel, na, nb);
+  mx_order<16, 8>();
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mx_mfma(f.a[i], f.b[j], acc[i][j], sa[i], sb[j], t);
-    if (t < 3) f = fn;
+  for (int i = 0; i < 4; ++i) {
+    sa[i] = na[i];
+    sb[i] = nb[i];
   }
 }
 
@@ -225,15 +279,21 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_mx_gemm(MxGemmArgs g) {
   __shared__ __align__(16) uint8_t buf0[kMxStage];
   __shared__ __align__(16) uint8_t buf1[kMxStage];
   const int64_t ntm = g.M / 256, ntn = g.N / 256, ntiles = ntm * ntn;
-  // tiles in row-major order, a contiguous run per XCD (workgroups are
-  // dealt to the eight XCDs in turn), so an XCD's concurrent tiles share A rows
+  // Workgroups are dealt to the eight XCDs in turn; each XCD takes a
+  // contiguous run u of an order that walks bands of four tile rows column
+  // by column, so the 32 tiles an XCD runs at once form a 4 x 8 block: per
+  // K-step they need 4 slices of A and 8 of B from its L2 instead of 1 and 32.
   const int64_t per_xcd = (ntiles + 7) / 8;
-  const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (t >= ntiles) return;
-  const int64_t m0 = (t / ntn) * 256, n0 = (t % ntn) * 256;
+  const int64_t u = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (u >= ntiles) return;
+  constexpr int64_t kBand = 4;
+  const int64_t band = u / (kBand * ntn), rem = u % (kBand * ntn);
+  const int64_t band_rows = min<int64_t>(kBand, ntm - band * kBand);
+  const int64_t m0 = (band * kBand + rem % band_rows) * 256, n0 = (rem / band_rows) * 256;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, gq = lane >> 5;
+  const uint32_t sel = gq ? 0x07050301u : 0x06040200u;
 
   floatx16 acc[4][4];
 #pragma unroll
@@ -243,20 +303,21 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_mx_gemm(MxGemmArgs g) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) acc[i][j][k] = 0.f;
 
-  const int64_t nk = g.K / kMxBK;
+  const int64_t nk = g.K / kMxBK;  // >= 1
   mx_issue(g, m0, n0, 0, buf0);
   __syncthreads();  // waits for this wave's loads (vmcnt(0)), then for every wave
   if (nk > 1) mx_issue(g, m0, n0, kMxBK, buf1);
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    uint8_t* cur = (kt & 1) ? buf1 : buf0;
-    MxFrag f;
-    mx_read(cur, wm, wn, r, gq, 0, f);
-    mx_stage(cur, wm, wn, r, gq, f, acc);
-    // every wave is done reading cur and its own loads of the next stage
-    // have landed; then the stage after that streams into cur
-    __syncthreads();
-    if (kt + 2 < nk) mx_issue(g, m0, n0, (kt + 2) * kMxBK, cur);
+  MxFrag f;
+  uint32_t sa[4], sb[4];
+  mx_read(buf0, wm, wn, r, gq, 0, f);
+  mx_read_scales(buf0, wm, wn, r, sel, sa, sb);
+  int64_t kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    mx_stage(g, m0, n0, kt + 2 < nk, (kt + 2) * kMxBK, buf0, buf1, f, sa, sb, acc, wm, wn, r, gq, sel);
+    // on the last stage the reads of buf0 at its end are of stale data and unused
+    mx_stage(g, m0, n0, kt + 3 < nk, (kt + 3) * kMxBK, buf1, buf0, f, sa, sb, acc, wm, wn, r, gq, sel);
   }
+  if (kt < nk) mx_stage(g, m0, n0, false, 0, buf0, buf1, f, sa, sb, acc, wm, wn, r, gq, sel);
 
   // D layout of the 32 x 32 MFMA: lane l, value k -> column l % 32, row
   // 8 * (k / 4) + 4 * (l / 32) + k % 4
@@ -331,7 +392,8 @@ void launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t r
 }
 
 void launch_mx_gemm(const MxGemmArgs& g, hipStream_t st) {
-  const bool fast = g.M % 256 == 0 && g.N % 256 == 0 && g.K % kMxBK == 0 && (uintptr_t)g.a_codes % 16 == 0 &&
+  const bool fast = g.M % 256 == 0 && g.N % 256 == 0 && g.K % kMxBK == 0 && g.K <= (INT64_C(1) << 24) &&
+                    (uintptr_t)g.a_codes % 16 == 0 &&
                     (uintptr_t)g.b_codes % 16 == 0 && (uintptr_t)g.a_scales % 8 == 0 &&
                     (uintptr_t)g.b_scales % 8 == 0;
   if (fast) {
