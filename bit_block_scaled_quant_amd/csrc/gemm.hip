@@ -562,7 +562,9 @@ void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
                        ((uintptr_t)g.b_codes % 16 == 0) && ((uintptr_t)g.a_scales % 8 == 0) &&
                        ((uintptr_t)g.b_scales % 8 == 0);
   if (aligned && g.M % 256 == 0 && g.N % 256 == 0 && g.K % (2 * kDirBK) == 0 &&
-      g.K <= (INT64_C(1) << 26) && (uintptr_t)g.a_scales % 4 == 0 && (uintptr_t)g.b_scales % 4 == 0) {
+      g.K <= (INT64_C(1) << 24) && (uintptr_t)g.a_scales % 4 == 0 && (uintptr_t)g.b_scales % 4 == 0) {
+    // (K <= 2^24 keeps the 32-bit byte offsets of m32_issue, up to 255 rows
+    // of K / 2 bytes, below 2^31)
     // Whole waves of 256 x 256 tiles (one workgroup per CU); when the last
     // wave would be at most half full, its tiles run as 256 x 128 halves
     // instead, so that wave takes about half as long.
