@@ -3,7 +3,8 @@
 A thin ctypes binding over ``libnvfp4.so`` (C ABI in ``include/nvfp4.h``).
 The functions named like the C entry points (``nvfp4_quantize``,
 ``nvfp4_quantize_2d``, ``nvfp4_quantize_cast_transpose``, ``nvfp4_rht``,
-``nvfp4_dequantize``, ``nvfp4_gemm``, and ``mxfp4_quantize``,
+``nvfp4_dequantize``, ``nvfp4_gemm``, ``nvfp4_gemm_ex``,
+``nvfp4_quantize_with_amax``, and ``mxfp4_quantize``,
 ``mxfp4_dequantize``, ``mxfp4_gemm``) only marshal torch
 tensors into pointers and the current HIP stream; every step of the
 computation runs in the library's HIP kernels.  There is no CPU fallback: if
@@ -64,6 +65,10 @@ def lib():
         L.nvfp4_dequantize.argtypes = [P, P, P, I64, I64, I, P, P]
         L.nvfp4_gemm.restype = I
         L.nvfp4_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, P]
+        L.nvfp4_gemm_ex.restype = I
+        L.nvfp4_gemm_ex.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, I, ctypes.c_float, P, P]
+        L.nvfp4_quantize_with_amax.restype = I
+        L.nvfp4_quantize_with_amax.argtypes = [P, I, I64, I64, I, U64, I, U64, P, P, P, P]
         L.mxfp4_quantize.restype = I
         L.mxfp4_quantize.argtypes = [P, I, I64, I64, P, P, P]
         L.mxfp4_dequantize.restype = I
@@ -147,6 +152,20 @@ def nvfp4_gemm(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_sc
     _check(lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_codes),
                             _ptr(b_scales), _ptr(b_tensor_scale), int(M), int(N), int(K), _ptr(c),
                             _stream(c)), "nvfp4_gemm")
+
+
+def nvfp4_gemm_ex(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, M, N, K, c,
+                  beta=0.0, c_amax=None):
+    _check(lib().nvfp4_gemm_ex(_ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_codes),
+                               _ptr(b_scales), _ptr(b_tensor_scale), int(M), int(N), int(K), _ptr(c),
+                               _dtype(c), float(beta), _ptr(c_amax), _stream(c)), "nvfp4_gemm_ex")
+
+
+def nvfp4_quantize_with_amax(x, rounding, seed, rht, rht_seed, codes, scales, tensor_scale):
+    rows, cols = x.shape
+    _check(lib().nvfp4_quantize_with_amax(_ptr(x), _dtype(x), rows, cols, int(rounding), int(seed), int(rht),
+                                          int(rht_seed), _ptr(codes), _ptr(scales), _ptr(tensor_scale),
+                                          _stream(x)), "nvfp4_quantize_with_amax")
 
 
 def mxfp4_quantize(x, codes, scales):
@@ -281,4 +300,16 @@ def mx_gemm(a: MxQuantized, b: MxQuantized, out=None):
         raise ValueError(f"K mismatch: {K} vs {K2}")
     c = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=a.codes.device)
     mxfp4_gemm(a.codes, a.scales, b.codes, b.scales, M, N, K, c)
+    return c
+
+
+def gemm_ex(a: Quantized, b: Quantized, out=None, dtype=torch.float32, beta=0.0, amax=None):
+    """C = deq(a) . deq(b)^T + beta * C (fp32 or bf16 C); when amax (a 1-element
+    float32 device tensor) is given it receives max |C|."""
+    M, K = a.shape
+    N, K2 = b.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: {K} vs {K2}")
+    c = out if out is not None else torch.empty(M, N, dtype=dtype, device=a.codes.device)
+    nvfp4_gemm_ex(a.codes, a.scales, a.tensor_scale, b.codes, b.scales, b.tensor_scale, M, N, K, c, beta, amax)
     return c

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <cmath>
 
 #include "../../include/nvfp4.h"
 #include "internal.hpp"
@@ -106,6 +107,21 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int rou
   return check_launch("nvfp4_quantize");
 }
 
+int nvfp4_quantize_with_amax(const void* x, int dtype, int64_t rows, int64_t cols, int rounding, uint64_t seed,
+                             int rht, uint64_t rht_seed, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                             void* stream) {
+  int st = validate_quant(x, dtype, rows, cols, rounding, codes, scales, tensor_scale, nullptr, nullptr);
+  if (st) return st;
+  if (rht != 0 && rht != 1) return NVFP4_ERR_ARG;
+  int cus = 0;
+  if ((st = device_cus(&cus))) return st;
+  nvfp4::QuantArgs a{x,       dtype == NVFP4_BF16, rows,    cols,   rounding,     seed,    rht == 1,
+                     rht ? nvfp4::rht_sign_mask(rht_seed) : 0u,   false, codes, scales, tensor_scale,
+                     nullptr, nullptr,             true};
+  nvfp4::launch_quantize(a, cus, (hipStream_t)stream);
+  return check_launch("nvfp4_quantize_with_amax");
+}
+
 int nvfp4_quantize_2d(const void* w, int dtype, int64_t rows, int64_t cols, int rounding, uint64_t seed,
                       uint8_t* codes, uint8_t* scales, float* tensor_scale, uint8_t* codes_t,
                       uint8_t* scales_t, void* stream) {
@@ -167,6 +183,30 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
   return check_launch("nvfp4_dequantize");
 }
 
+int nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+                  const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale, int64_t M,
+                  int64_t N, int64_t K, void* c, int c_dtype, float beta, float* c_amax, void* stream) {
+  if (!a_codes || !a_scales || !a_tensor_scale || !b_codes || !b_scales || !b_tensor_scale || !c)
+    return NVFP4_ERR_ARG;
+  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_ARG;
+  if (!(beta == beta) || beta == INFINITY || beta == -INFINITY) return NVFP4_ERR_ARG;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!size_ok(M, K) || !size_ok(N, K) || !size_ok(M, N)) return NVFP4_ERR_SHAPE;
+  if (M > INT64_C(65535) * 128) return NVFP4_ERR_SHAPE;  // grid.y limit
+  if (!aligned(a_codes, 8) || !aligned(b_codes, 8) || !aligned(c, c_dtype == NVFP4_F32 ? 4 : 2) ||
+      !aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4) || (c_amax && !aligned(c_amax, 4)))
+    return NVFP4_ERR_ALIGN;
+  int cus = 0;
+  int st = device_cus(&cus);
+  if (st) return st;
+  const bool f32 = c_dtype == NVFP4_F32;
+  nvfp4::GemmArgs g{a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, M, N, K,
+                    f32 ? static_cast<float*>(c) : nullptr, f32 ? nullptr : static_cast<uint16_t*>(c), beta,
+                    reinterpret_cast<unsigned*>(c_amax)};
+  nvfp4::launch_gemm(g, cus, (hipStream_t)stream);
+  return check_launch("nvfp4_gemm_ex");
+}
+
 int mxfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                    void* stream) {
   if (!x || !codes || !scales) return NVFP4_ERR_ARG;
@@ -219,7 +259,8 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_t
   int cus = 0;
   int st = device_cus(&cus);
   if (st) return st;
-  nvfp4::GemmArgs g{a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, M, N, K, c};
+  nvfp4::GemmArgs g{a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, M, N, K, c, nullptr,
+                    0.0f,    nullptr};
   nvfp4::launch_gemm(g, cus, (hipStream_t)stream);
   return check_launch("nvfp4_gemm");
 }

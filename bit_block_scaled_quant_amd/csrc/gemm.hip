@@ -176,6 +176,40 @@ __device__ __forceinline__ void stage_store(GemmStage<BM, BN>& sm, const Staged<
   }
 }
 
+// ---- epilogue -------------------------------------------------------------
+// One output element: v = (acc / S_a) / S_b as two multiplies by the
+// reciprocals; with beta != 0, v + beta * C_old (C_old as stored, fp32 or
+// bf16); stored as fp32, or rounded to nearest-even bf16.  m collects
+// |stored value| for the optional output amax.
+__device__ __forceinline__ void store_c(const GemmArgs& g, int64_t idx, float v, float& m, bool streaming) {
+  if (g.c16) {
+    if (g.beta != 0.0f) v = v + g.beta * __uint_as_float((uint32_t)g.c16[idx] << 16);
+    const uint32_t h = bf16_rne(v);
+    g.c16[idx] = (uint16_t)h;
+    m = fmaxf(m, fabsf(__uint_as_float(h << 16)));
+  } else {
+    if (g.beta != 0.0f) v = v + g.beta * g.c[idx];
+    if (streaming)
+      __builtin_nontemporal_store(v, &g.c[idx]);  // written once, not read here (+2.5% measured)
+    else
+      g.c[idx] = v;
+    m = fmaxf(m, fabsf(v));
+  }
+}
+
+// the wave's maximum into *g.amax (float bits; non-negative floats order
+// like their bit patterns); the atomic only when it can raise the value
+__device__ __forceinline__ void amax_to(const GemmArgs& g, float m) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) {
+    const unsigned bits = __float_as_uint(m);
+    if (bits > __hip_atomic_load(g.amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(g.amax, bits);
+  }
+}
+
+__global__ void k_zero_amax(unsigned* p) { *p = 0u; }
+
 // ---- the kernel ---------------------------------------------------------
 // BM x BN tile per workgroup, (BM/2) x (BN/2) per wave.
 template <int BM, int BN, bool ALIGNED>
@@ -246,6 +280,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 
   // epilogue: C = acc / (S_a * S_b), lane holds rows 4*lg .. 4*lg+3 of column li
   const float inv_a = __fdiv_rn(1.0f, g.a_ts[0]), inv_b = __fdiv_rn(1.0f, g.b_ts[0]);
+  float cmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
 #pragma unroll
@@ -255,10 +290,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t m = m0 + wm * (BM / 2) + i * 16 + lg * 4 + r;
-        if (m < g.M) g.c[m * g.N + n] = (acc[i][j][r] * inv_a) * inv_b;
+        if (m < g.M) store_c(g, m * g.N + n, (acc[i][j][r] * inv_a) * inv_b, cmax, false);
       }
     }
   }
+  if (g.amax) amax_to(g, cmax);
 }
 
 // ---- fast path: direct-to-LDS stages, 32 x 32 x 16 MFMA, pipelined unpack --
@@ -500,7 +536,10 @@ __device__ __forceinline__ void m32_stage(const GemmArgs& g, int64_t m0, int64_t
 
 // Workgroup u computes columns (u % (4 / NT)) * 64 NT .. of the 256 x 256
 // tile tile0 + u / (4 / NT) (tiles in row-major order, N / 256 per row).
-template <int NT>
+// EX: the epilogue options of nvfp4_gemm_ex (bf16 output, beta, output
+// amax); without them the plain fp32 epilogue, compiled on its own so that
+// the main loop's register allocation is the same as for nvfp4_gemm.
+template <int NT, bool EX>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_t tile0) {
   using L = M32<NT>;
   __shared__ __align__(16) uint8_t buf0[L::kStage];
@@ -540,6 +579,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_
   // D layout of the 32 x 32 MFMA: lane l, value k -> column l % 32, row
   // 8 * (k / 4) + 4 * (l / 32) + k % 4
   const float inv_a = __fdiv_rn(1.0f, g.a_ts[0]), inv_b = __fdiv_rn(1.0f, g.b_ts[0]);
+  float cmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -548,15 +588,33 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int64_t m = m0 + wm * 128 + i * 32 + 8 * (k >> 2) + 4 * gq + (k & 3);
-        // streaming store: C is written once and not read here (+2.5% measured)
-        __builtin_nontemporal_store((acc[i][j][k] * inv_a) * inv_b, &g.c[m * g.N + n]);
+        if (EX)
+          store_c(g, m * g.N + n, (acc[i][j][k] * inv_a) * inv_b, cmax, true);
+        else  // streaming store: C is written once and not read here (+2.5% measured)
+          __builtin_nontemporal_store((acc[i][j][k] * inv_a) * inv_b, &g.c[m * g.N + n]);
       }
     }
+  }
+  if (EX && g.amax) amax_to(g, cmax);
+}
+
+// Whole waves of 256 x 256 tiles (one workgroup per CU); when the last wave
+// would be at most half full, its tiles run as 256 x 128 halves instead, so
+// that wave takes about half as long.
+template <bool EX>
+static void launch_m32(const GemmArgs& g, int64_t ntiles, int64_t full, int64_t rem, int64_t c, hipStream_t st) {
+  if (rem == 0 || 2 * rem > c) {
+    hipLaunchKernelGGL((k_gemm_m32<4, EX>), dim3((unsigned)ntiles), dim3(kGemmThreads), 0, st, g, INT64_C(0));
+  } else {
+    if (full > 0)
+      hipLaunchKernelGGL((k_gemm_m32<4, EX>), dim3((unsigned)full), dim3(kGemmThreads), 0, st, g, INT64_C(0));
+    hipLaunchKernelGGL((k_gemm_m32<2, EX>), dim3((unsigned)(2 * rem)), dim3(kGemmThreads), 0, st, g, full);
   }
 }
 
 void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
   constexpr int BM = 256, BN = 256;
+  if (g.amax) hipLaunchKernelGGL(k_zero_amax, dim3(1), dim3(1), 0, st, g.amax);
   const dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM));
   const bool aligned = g.K % kBK == 0 && ((uintptr_t)g.a_codes % 16 == 0) &&
                        ((uintptr_t)g.b_codes % 16 == 0) && ((uintptr_t)g.a_scales % 8 == 0) &&
@@ -565,19 +623,13 @@ void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
       g.K <= (INT64_C(1) << 24) && (uintptr_t)g.a_scales % 4 == 0 && (uintptr_t)g.b_scales % 4 == 0) {
     // (K <= 2^24 keeps the 32-bit byte offsets of m32_issue, up to 255 rows
     // of K / 2 bytes, below 2^31)
-    // Whole waves of 256 x 256 tiles (one workgroup per CU); when the last
-    // wave would be at most half full, its tiles run as 256 x 128 halves
-    // instead, so that wave takes about half as long.
     const int64_t ntiles = (g.M / 256) * (g.N / 256);
     const int64_t c = std::max(cus, 1);
     const int64_t full = (ntiles / c) * c, rem = ntiles - full;
-    if (rem == 0 || 2 * rem > c) {
-      hipLaunchKernelGGL(k_gemm_m32<4>, dim3((unsigned)ntiles), dim3(kGemmThreads), 0, st, g, INT64_C(0));
-    } else {
-      if (full > 0)
-        hipLaunchKernelGGL(k_gemm_m32<4>, dim3((unsigned)full), dim3(kGemmThreads), 0, st, g, INT64_C(0));
-      hipLaunchKernelGGL(k_gemm_m32<2>, dim3((unsigned)(2 * rem)), dim3(kGemmThreads), 0, st, g, full);
-    }
+    if (g.c16 || g.beta != 0.0f || g.amax)
+      launch_m32<true>(g, ntiles, full, rem, c, st);
+    else
+      launch_m32<false>(g, ntiles, full, rem, c, st);
   } else if (aligned) {
     hipLaunchKernelGGL((k_gemm<BM, BN, true>), grid, dim3(kGemmThreads), 0, st, g);
   } else {

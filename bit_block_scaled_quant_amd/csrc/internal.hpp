@@ -22,6 +22,7 @@ struct QuantArgs {
   float* tensor_scale;
   uint8_t* codes_t;  // may be null
   uint8_t* scales_t;
+  bool amax_given;   // tensor_scale[1] already holds the amax: skip pass 1
 };
 
 void launch_quantize(const QuantArgs& a, int cus, hipStream_t st);
@@ -58,7 +59,10 @@ struct GemmArgs {
   const uint8_t* b_scales;
   const float* b_ts;
   int64_t M, N, K;
-  float* c;
+  float* c;            // fp32 output, or
+  uint16_t* c16;       // bf16 output (exactly one of c, c16 is set)
+  float beta;          // C = A.B^T + beta * C_old (C_old not read when beta == 0)
+  unsigned* amax;      // optional: max |stored C| as float bits (cleared by launch_gemm)
 };
 
 void launch_gemm(const GemmArgs& g, int cus, hipStream_t st);

@@ -923,11 +923,13 @@ static void launch_tile(const QuantArgs& a, bool two_d, int cus, hipStream_t st)
 
 template <bool BF16>
 static void launch_quantize_t(const QuantArgs& a, int cus, hipStream_t st) {
-  hipLaunchKernelGGL(k_init_amax, dim3(1), dim3(1), 0, st, a.tensor_scale);
-  if (a.rht)
-    launch_amax<BF16, true>(a, cus, st);
-  else
-    launch_amax<BF16, false>(a, cus, st);
+  if (!a.amax_given) {
+    hipLaunchKernelGGL(k_init_amax, dim3(1), dim3(1), 0, st, a.tensor_scale);
+    if (a.rht)
+      launch_amax<BF16, true>(a, cus, st);
+    else
+      launch_amax<BF16, false>(a, cus, st);
+  }
   const bool sr = a.rounding == 1;
   if (a.two_d || a.codes_t) {
     if (sr)

@@ -200,6 +200,37 @@ int mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, 
 int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* c, void* stream);
 
+/*
+ * nvfp4_gemm with epilogue options (for a training step: gradient
+ * accumulation, a 16-bit output, and the amax the next quantization needs):
+ *   C [M][N] = deq(A) . deq(B)^T + beta * C_old, where the product term is
+ *   computed as nvfp4_gemm does (fp32, then times 1/S_a and 1/S_b), C_old is
+ *   read only when beta != 0, and the sum is one fp32 add of the rounded
+ *   beta * C_old;
+ *   c_dtype NVFP4_F32 stores fp32, NVFP4_BF16 the fp32 result rounded to
+ *   nearest-even bf16 (C_old is then read as bf16);
+ *   c_amax (NULL or a device float): set to max |stored C| over the call,
+ *   so a following nvfp4_quantize_with_amax of C can skip its amax pass.
+ * Shapes as nvfp4_gemm.  beta must be finite.  Alignment: codes 8 bytes, C 4
+ * (fp32) or 2 (bf16) bytes, c_amax 4 bytes.
+ */
+int nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+                  const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale,
+                  int64_t M, int64_t N, int64_t K, void* c, int c_dtype, float beta, float* c_amax,
+                  void* stream);
+
+/*
+ * nvfp4_quantize without its first pass: tensor_scale[1] must already hold
+ * the amax that nvfp4_quantize would compute (of x, or of its transform
+ * when rht = 1), e.g. the c_amax of the nvfp4_gemm_ex that produced x.
+ * With that amax the outputs are bit-identical to nvfp4_quantize's, from a
+ * single read of x.  No transposed copy.  Arguments otherwise as
+ * nvfp4_quantize.
+ */
+int nvfp4_quantize_with_amax(const void* x, int dtype, int64_t rows, int64_t cols, int rounding,
+                             uint64_t seed, int rht, uint64_t rht_seed, uint8_t* codes,
+                             uint8_t* scales, float* tensor_scale, void* stream);
+
 /* Static text for a status code. */
 const char* nvfp4_status_string(int status);
 /* Text of the last NVFP4_ERR_HIP on the calling thread ("" if none). */

@@ -24,7 +24,8 @@ def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("nvfp4_quantize", "nvfp4_quantize_2d", "nvfp4_quantize_cast_transpose", "nvfp4_rht",
               "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error",
-              "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm"):
+              "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm", "nvfp4_gemm_ex",
+              "nvfp4_quantize_with_amax"):
         assert n in names
 
 
@@ -120,6 +121,22 @@ def test_mx_calls_reject_bad_arguments():
     assert g(A16, A16, A16, A16, 0, 16, 64, A16, None) == -2
     assert g(None, A16, A16, A16, 16, 16, 64, A16, None) == -1
     assert g(A8, A16, A16, A16, 16, 16, 64, A16, None) == -3    # codes 16-byte aligned
+
+
+def test_gemm_ex_and_quantize_with_amax_reject_bad_arguments():
+    L = nv.lib()
+    g = L.nvfp4_gemm_ex
+    F = ctypes.c_float
+    assert g(A16, A16, A16, A16, A16, A16, 16, 16, 32, A16, 2, F(0.0), None, None) == -1   # C dtype
+    assert g(A16, A16, A16, A16, A16, A16, 16, 16, 32, A16, 0, F(float("nan")), None, None) == -1
+    assert g(A16, A16, A16, A16, A16, A16, 16, 16, 32, A16, 0, F(float("inf")), None, None) == -1
+    assert g(A16, A16, A16, A16, A16, A16, 16, 16, 24, A16, 0, F(0.0), None, None) == -2
+    assert g(A16, A16, A16, A16, A16, A16, 16, 16, 32, ctypes.c_void_p(0x10002), 0, F(0.0), None, None) == -3
+    assert g(A16, A16, A16, A16, A16, A16, 16, 16, 32, A16, 0, F(0.0), ctypes.c_void_p(0x10002), None) == -3
+    q = L.nvfp4_quantize_with_amax
+    assert q(A16, 1, 4, 24, 0, 0, 0, 0, A16, A16, A16, None) == -2
+    assert q(A16, 1, 4, 32, 0, 0, 2, 0, A16, A16, A16, None) == -1
+    assert q(None, 1, 4, 32, 0, 0, 0, 0, A16, A16, A16, None) == -1
 
 
 def test_rht_and_gemm_reject_bad_arguments():
