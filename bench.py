@@ -256,6 +256,17 @@ def main():
     # outside the step: dequantization of dY's rowwise copy (HBM-bound)
     extras = {}
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gemm_flops_one = 2.0 * TOKENS * FFN * HIDDEN
+
+    def timed_ms_ev(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
     for dt, out_bytes, tag in ((torch.bfloat16, 2, "bf16"), (torch.float32, 4, "f32")):
         out_t = torch.empty(TOKENS, FFN, dtype=dt, device=dev)
 
@@ -273,6 +284,22 @@ def main():
         extras[f"dequantize_dY_{tag}"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
                                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         del out_t
+
+    # epilogue options: fprop with bf16 output and the output amax, then the
+    # single-read quantization of that output (its amax already known)
+    Y16 = torch.empty(TOKENS, FFN, dtype=torch.bfloat16, device=dev)
+    tsY = torch.zeros(2, dtype=torch.float32, device=dev)
+    ms = timed_ms_ev(lambda: nv.gemm_ex(qX, qW, out=Y16, amax=tsY[1:]))
+    tf = gemm_flops_one / (ms * 1e-3) / 1e12
+    extras["gemm_ex_fprop_bf16_out_amax"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                                             "frac_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+    qY = nv.Quantized(torch.empty(TOKENS, FFN // 2, dtype=torch.uint8, device=dev),
+                      torch.empty(TOKENS, FFN // 16, dtype=torch.uint8, device=dev), tsY)
+    ms = timed_ms_ev(lambda: nv.nvfp4_quantize_with_amax(Y16, 0, 0, 0, 0, qY.codes, qY.scales, tsY))
+    gbs = TOKENS * FFN * (2 + 0.5 + 1.0 / 16.0) / (ms * 1e-3) / 1e9
+    extras["quantize_with_amax_Y_bf16"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
+                                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del Y16, qY
 
     # MXFP4, the format the pages measure NVFP4 against: the same three GEMMs
     # on gfx950's scaled FP4 MFMA, its quantizer, and the quantization error
