@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--extras", choices=("all", "none", "only"), default="all",
+                   help="measurements outside the step (dequantize, MXFP4, epilogue options): "
+                        "all (default), none, or only those (one untimed step first; prints "
+                        "just the extras)")
     p.add_argument("--composed", action="store_true",
                    help="quantize X^T and dY^T by separate calls on materialized transposes "
                         "instead of the cast-transpose")
@@ -231,6 +235,112 @@ def main():
             if events is not None:
                 events[i][1].record()
 
+    def run_extras():
+        """Measurements outside the step (not part of value)."""
+        # outside the step: dequantization of dY's rowwise copy (HBM-bound)
+        extras = {}
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gemm_flops_one = 2.0 * TOKENS * FFN * HIDDEN
+
+        def timed_ms_ev(fn, reps=10):
+            fn()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(reps):
+                fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / reps
+        for dt, out_bytes, tag in ((torch.bfloat16, 2, "bf16"), (torch.float32, 4, "f32")):
+            out_t = torch.empty(TOKENS, FFN, dtype=dt, device=dev)
+
+            def deq():
+                nv.nvfp4_dequantize(qdY.codes, qdY.scales, qdY.tensor_scale, TOKENS, FFN, out_t)
+            deq()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(10):
+                deq()
+            ev1.record()
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / 10
+            gbs = TOKENS * FFN * (0.5 + 1.0 / 16.0 + out_bytes) / (ms * 1e-3) / 1e9
+            extras[f"dequantize_dY_{tag}"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
+                                              "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            del out_t
+
+        # epilogue options: fprop with bf16 output and the output amax, then the
+        # single-read quantization of that output (its amax already known)
+        Y16 = torch.empty(TOKENS, FFN, dtype=torch.bfloat16, device=dev)
+        tsY = torch.zeros(2, dtype=torch.float32, device=dev)
+        ms = timed_ms_ev(lambda: nv.gemm_ex(qX, qW, out=Y16, amax=tsY[1:]))
+        tf = gemm_flops_one / (ms * 1e-3) / 1e12
+        extras["gemm_ex_fprop_bf16_out_amax"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                                                 "frac_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+        qY = nv.Quantized(torch.empty(TOKENS, FFN // 2, dtype=torch.uint8, device=dev),
+                          torch.empty(TOKENS, FFN // 16, dtype=torch.uint8, device=dev), tsY)
+        ms = timed_ms_ev(lambda: nv.nvfp4_quantize_with_amax(Y16, 0, 0, 0, 0, qY.codes, qY.scales, tsY))
+        gbs = TOKENS * FFN * (2 + 0.5 + 1.0 / 16.0) / (ms * 1e-3) / 1e9
+        extras["quantize_with_amax_Y_bf16"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
+                                               "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del Y16, qY
+
+        # MXFP4, the format the pages measure NVFP4 against: the same three GEMMs
+        # on gfx950's scaled FP4 MFMA, its quantizer, and the quantization error
+        # of both formats on the layer's tensors (a dataset-free proxy for the
+        # pages' accuracy comparison).  Outside the step.
+        def timed_ms(fn, reps=10):
+            fn()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(reps):
+                fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / reps
+
+        Wt = W.t().contiguous()
+        dYt_m = dY.t().contiguous()
+        Xt_m = X.t().contiguous()
+        mx_ops = {"fprop": (X, W), "dgrad": (dY, Wt), "wgrad": (dYt_m, Xt_m)}
+        mxq = {}
+        for name, (a, b) in mx_ops.items():
+            qa, qb = nv.mx_quantize(a), nv.mx_quantize(b)
+            M, K = a.shape
+            N = b.shape[0]
+            cbuf = {"fprop": Y, "dgrad": dX, "wgrad": dW}[name]
+            ms = timed_ms(lambda: nv.mx_gemm(qa, qb, out=cbuf))
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            extras[f"mxfp4_gemm_{name}"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                                            "frac_fp4_mfma_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
+            mxq[name] = (qa, M, K)
+        qa, M, K = mxq["dgrad"]
+        ms = timed_ms(lambda: nv.mxfp4_quantize(dY, qa.codes, qa.scales))
+        gbs = M * K * (2 + 0.5 + 1.0 / 32.0) / (ms * 1e-3) / 1e9
+        extras["mxfp4_quantize_dY"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
+                                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del Wt, dYt_m, Xt_m, mxq, qa
+
+        def rel_err(t, deq):
+            d = (deq.double() - t.double())
+            return float(torch.linalg.vector_norm(d) / torch.linalg.vector_norm(t.double()))
+
+        err = {}
+        for name, t, two_d in (("X", X, False), ("W", W, True), ("dY", dY, False)):
+            qn = nv.quantize_2d(t, transposed=False) if two_d else nv.quantize(t)
+            e_nv = rel_err(t, nv.dequantize(qn))
+            del qn
+            e_mx = rel_err(t, nv.mx_dequantize(nv.mx_quantize(t)))
+            err[name] = {"nvfp4": round(e_nv, 5), "mxfp4": round(e_mx, 5)}
+        extras["relative_rms_quantization_error"] = err
+        return extras
+
+    if args.extras == "only":
+        step()
+        torch.cuda.synchronize()
+        print(json.dumps({"extras": run_extras()}), flush=True)
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -253,102 +363,7 @@ def main():
         for (name, _, _, _), (a, b) in zip(calls, ev):
             per_call[name].append(a.elapsed_time(b))
 
-    # outside the step: dequantization of dY's rowwise copy (HBM-bound)
-    extras = {}
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    gemm_flops_one = 2.0 * TOKENS * FFN * HIDDEN
-
-    def timed_ms_ev(fn, reps=10):
-        fn()
-        torch.cuda.synchronize()
-        ev0.record()
-        for _ in range(reps):
-            fn()
-        ev1.record()
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / reps
-    for dt, out_bytes, tag in ((torch.bfloat16, 2, "bf16"), (torch.float32, 4, "f32")):
-        out_t = torch.empty(TOKENS, FFN, dtype=dt, device=dev)
-
-        def deq():
-            nv.nvfp4_dequantize(qdY.codes, qdY.scales, qdY.tensor_scale, TOKENS, FFN, out_t)
-        deq()
-        torch.cuda.synchronize()
-        ev0.record()
-        for _ in range(10):
-            deq()
-        ev1.record()
-        torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1) / 10
-        gbs = TOKENS * FFN * (0.5 + 1.0 / 16.0 + out_bytes) / (ms * 1e-3) / 1e9
-        extras[f"dequantize_dY_{tag}"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
-                                          "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-        del out_t
-
-    # epilogue options: fprop with bf16 output and the output amax, then the
-    # single-read quantization of that output (its amax already known)
-    Y16 = torch.empty(TOKENS, FFN, dtype=torch.bfloat16, device=dev)
-    tsY = torch.zeros(2, dtype=torch.float32, device=dev)
-    ms = timed_ms_ev(lambda: nv.gemm_ex(qX, qW, out=Y16, amax=tsY[1:]))
-    tf = gemm_flops_one / (ms * 1e-3) / 1e12
-    extras["gemm_ex_fprop_bf16_out_amax"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
-                                             "frac_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
-    qY = nv.Quantized(torch.empty(TOKENS, FFN // 2, dtype=torch.uint8, device=dev),
-                      torch.empty(TOKENS, FFN // 16, dtype=torch.uint8, device=dev), tsY)
-    ms = timed_ms_ev(lambda: nv.nvfp4_quantize_with_amax(Y16, 0, 0, 0, 0, qY.codes, qY.scales, tsY))
-    gbs = TOKENS * FFN * (2 + 0.5 + 1.0 / 16.0) / (ms * 1e-3) / 1e9
-    extras["quantize_with_amax_Y_bf16"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
-                                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-    del Y16, qY
-
-    # MXFP4, the format the pages measure NVFP4 against: the same three GEMMs
-    # on gfx950's scaled FP4 MFMA, its quantizer, and the quantization error
-    # of both formats on the layer's tensors (a dataset-free proxy for the
-    # pages' accuracy comparison).  Outside the step.
-    def timed_ms(fn, reps=10):
-        fn()
-        torch.cuda.synchronize()
-        ev0.record()
-        for _ in range(reps):
-            fn()
-        ev1.record()
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / reps
-
-    Wt = W.t().contiguous()
-    dYt_m = dY.t().contiguous()
-    Xt_m = X.t().contiguous()
-    mx_ops = {"fprop": (X, W), "dgrad": (dY, Wt), "wgrad": (dYt_m, Xt_m)}
-    mxq = {}
-    for name, (a, b) in mx_ops.items():
-        qa, qb = nv.mx_quantize(a), nv.mx_quantize(b)
-        M, K = a.shape
-        N = b.shape[0]
-        cbuf = {"fprop": Y, "dgrad": dX, "wgrad": dW}[name]
-        ms = timed_ms(lambda: nv.mx_gemm(qa, qb, out=cbuf))
-        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        extras[f"mxfp4_gemm_{name}"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
-                                        "frac_fp4_mfma_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
-        mxq[name] = (qa, M, K)
-    qa, M, K = mxq["dgrad"]
-    ms = timed_ms(lambda: nv.mxfp4_quantize(dY, qa.codes, qa.scales))
-    gbs = M * K * (2 + 0.5 + 1.0 / 32.0) / (ms * 1e-3) / 1e9
-    extras["mxfp4_quantize_dY"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
-                                   "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-    del Wt, dYt_m, Xt_m, mxq, qa
-
-    def rel_err(t, deq):
-        d = (deq.double() - t.double())
-        return float(torch.linalg.vector_norm(d) / torch.linalg.vector_norm(t.double()))
-
-    err = {}
-    for name, t, two_d in (("X", X, False), ("W", W, True), ("dY", dY, False)):
-        qn = nv.quantize_2d(t, transposed=False) if two_d else nv.quantize(t)
-        e_nv = rel_err(t, nv.dequantize(qn))
-        del qn
-        e_mx = rel_err(t, nv.mx_dequantize(nv.mx_quantize(t)))
-        err[name] = {"nvfp4": round(e_nv, 5), "mxfp4": round(e_mx, 5)}
-    extras["relative_rms_quantization_error"] = err
+    extras = run_extras() if args.extras == "all" else {}
 
     gemm_flops = 2.0 * TOKENS * FFN * HIDDEN
     step_flops = 3 * gemm_flops
