@@ -534,20 +534,42 @@ __device__ __forceinline__ void m32_stage(const GemmArgs& g, int64_t m0, int64_t
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Workgroup u computes columns (u % (4 / NT)) * 64 NT .. of the 256 x 256
-// tile tile0 + u / (4 / NT) (tiles in row-major order, N / 256 per row).
+// Tiles are numbered in band order: bands of four tile rows, walked column
+// by column (u -> tile_mn), so that 32 consecutive tiles form a 4 x 8 block.
+// A launch covers tiles tile0 .. tile0 + ntl - 1 of that order.  With NT = 4
+// the workgroups are dealt to the eight XCDs in turn and each XCD takes a
+// contiguous run, so its 32 concurrent tiles share 4 slices of A and 8 of B
+// per K-step in its L2 (instead of about 36 distinct ones); with NT = 2 (the
+// last, partial wave) workgroup u computes columns (u % 2) * 128 .. of tile
+// tile0 + u / 2.
 // EX: the epilogue options of nvfp4_gemm_ex (bf16 output, beta, output
 // amax); without them the plain fp32 epilogue, compiled on its own so that
 // the main loop's register allocation is the same as for nvfp4_gemm.
+__device__ __forceinline__ void tile_mn(int64_t u, int64_t ntm, int64_t ntn, int64_t& m0, int64_t& n0) {
+  constexpr int64_t kBand = 4;
+  const int64_t band = u / (kBand * ntn), rem = u % (kBand * ntn);
+  const int64_t band_rows = min<int64_t>(kBand, ntm - band * kBand);
+  m0 = (band * kBand + rem % band_rows) * 256;
+  n0 = (rem / band_rows) * 256;
+}
+
 template <int NT, bool EX>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_t tile0) {
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_t tile0, int64_t ntl) {
   using L = M32<NT>;
   __shared__ __align__(16) uint8_t buf0[L::kStage];
   __shared__ __align__(16) uint8_t buf1[L::kStage];
-  constexpr int kSub = 4 / NT;
-  const int64_t ntn = g.N / 256;
-  const int64_t t = tile0 + blockIdx.x / kSub;
-  const int64_t m0 = (t / ntn) * 256, n0 = (t % ntn) * 256 + (blockIdx.x % kSub) * L::kBN;
+  const int64_t ntm = g.M / 256, ntn = g.N / 256;
+  int64_t u;
+  if (NT == 4) {
+    const int64_t per_xcd = (ntl + 7) / 8;
+    u = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (u >= ntl) return;  // the whole workgroup
+  } else {
+    u = blockIdx.x / 2;
+  }
+  int64_t m0, n0;
+  tile_mn(tile0 + u, ntm, ntn, m0, n0);
+  if (NT == 2) n0 += (blockIdx.x % 2) * L::kBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, gq = lane >> 5;
@@ -603,12 +625,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_
 // that wave takes about half as long.
 template <bool EX>
 static void launch_m32(const GemmArgs& g, int64_t ntiles, int64_t full, int64_t rem, int64_t c, hipStream_t st) {
+  const auto groups = [](int64_t n) { return (unsigned)(((n + 7) / 8) * 8); };
   if (rem == 0 || 2 * rem > c) {
-    hipLaunchKernelGGL((k_gemm_m32<4, EX>), dim3((unsigned)ntiles), dim3(kGemmThreads), 0, st, g, INT64_C(0));
+    hipLaunchKernelGGL((k_gemm_m32<4, EX>), dim3(groups(ntiles)), dim3(kGemmThreads), 0, st, g, INT64_C(0),
+                       ntiles);
   } else {
     if (full > 0)
-      hipLaunchKernelGGL((k_gemm_m32<4, EX>), dim3((unsigned)full), dim3(kGemmThreads), 0, st, g, INT64_C(0));
-    hipLaunchKernelGGL((k_gemm_m32<2, EX>), dim3((unsigned)(2 * rem)), dim3(kGemmThreads), 0, st, g, full);
+      hipLaunchKernelGGL((k_gemm_m32<4, EX>), dim3(groups(full)), dim3(kGemmThreads), 0, st, g, INT64_C(0),
+                         full);
+    hipLaunchKernelGGL((k_gemm_m32<2, EX>), dim3((unsigned)(2 * rem)), dim3(kGemmThreads), 0, st, g, full, rem);
   }
 }
 
