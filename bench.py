@@ -352,11 +352,11 @@ def main():
     run, graph_note = step, "eager launches"
     if args.graph:
         try:
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
+            warm = torch.cuda.Stream()
+            warm.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(warm):
                 step()
-            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.current_stream().wait_stream(warm)
             torch.cuda.synchronize()
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
