@@ -12,7 +12,9 @@
 //
 // Layout: a thread takes four consecutive elements (two code bytes, one
 // scale byte shared by four neighbouring threads), so a wave's store
-// instruction writes 1 KB (fp32) or 512 B (bf16) of contiguous output.
+// instruction writes 1 KB (fp32) or 512 B (bf16) of contiguous output, with
+// the nontemporal hint (measured 3.9 -> 6.0 TB/s for bf16, 4.4 -> 6.3 for fp32
+// on an 8192 x 20480 tensor).
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -44,11 +46,15 @@ __global__ __launch_bounds__(kDqThreads) void k_dequantize(const uint8_t* __rest
       const uint32_t c = (cw >> (4 * j)) & 15u;
       v[j] = __uint_as_float(__float_as_uint(tab[base + (c & 7u)]) | ((c & 8u) << 28));
     }
+    // streaming stores: the output is written once and not read here
     if (BF16OUT) {
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + 4 * q) =
-          make_uint2(bf16_rne(v[0]) | bf16_rne(v[1]) << 16, bf16_rne(v[2]) | bf16_rne(v[3]) << 16);
+      typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+      const u32x2_t w = {bf16_rne(v[0]) | bf16_rne(v[1]) << 16, bf16_rne(v[2]) | bf16_rne(v[3]) << 16};
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + 4 * q));
     } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(out) + 4 * q) = make_float4(v[0], v[1], v[2], v[3]);
+      typedef float f32x4_t __attribute__((ext_vector_type(4)));
+      const f32x4_t w = {v[0], v[1], v[2], v[3]};
+      __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + 4 * q));
     }
   }
 }
