@@ -45,10 +45,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--extras", choices=("all", "none", "only"), default="all",
-                   help="measurements outside the step (dequantize, MXFP4, epilogue options): "
-                        "all (default), none, or only those (one untimed step first; prints "
-                        "just the extras)")
+    p.add_argument("--extras", choices=("all", "none", "only", "sweep"), default="all",
+                   help="measurements outside the step (quantizer sweep, dequantize, MXFP4, "
+                        "epilogue options): all (default), none, only those (one untimed step "
+                        "first; prints just the extras), or only the quantizer sweep")
     p.add_argument("--graph", action="store_true",
                    help="time the step as replays of one HIP graph instead of eager launches "
                         "(measured +0.2%%: the launches already overlap)")
@@ -238,10 +238,49 @@ def main():
             if events is not None:
                 events[i][1].record()
 
+    def run_sweep(reps=5):
+        """The quantizer-only bandwidth sweep: bf16 N(0,1) with 0.1% of the
+        entries x100 at three shapes, each quantized 1D with its columnwise
+        copy and 2D with its transposed copy, with RNE and with SR.  Every
+        timed call starts from a cold cache: a 512 MiB write evicts the input
+        from L2 and the 256 MB MALL first.  The time is the median of the
+        calls (HIP events on the launch stream around the call alone)."""
+        flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev)
+        res = {}
+        for rows, cols in ((TOKENS, HIDDEN), (TOKENS, FFN), (4 * TOKENS, HIDDEN)):
+            xs = datagen.sweep(rows, cols, device=dev, seed=seed)
+            qs = alloc(rows, cols, True)
+            for two_d in (False, True):
+                for rnd in (0, 1):
+                    if two_d:
+                        fn = lambda: nv.nvfp4_quantize_2d(xs, rnd, seed, qs.codes, qs.scales,
+                                                          qs.tensor_scale, qs.codes_t, qs.scales_t)
+                    else:
+                        fn = lambda: nv.nvfp4_quantize(xs, rnd, seed, 0, 0, qs.codes, qs.scales,
+                                                       qs.tensor_scale, qs.codes_t, qs.scales_t)
+                    fn()
+                    ts = []
+                    for _ in range(reps):
+                        flush.fill_(float(len(ts)))
+                        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        a.record()
+                        fn()
+                        b.record()
+                        torch.cuda.synchronize()
+                        ts.append(a.elapsed_time(b))
+                    ms = float(np.median(ts))
+                    gbs = quant_bytes(rows, cols, 2, True) / (ms * 1e-3) / 1e9
+                    key = f"{rows}x{cols}_{'2d' if two_d else '1d'}+t_{'sr' if rnd else 'rne'}"
+                    res[key] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
+                                "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            del xs, qs
+        del flush
+        return res
+
     def run_extras():
         """Measurements outside the step (not part of value)."""
+        extras = {"quantizer_sweep": run_sweep()}
         # outside the step: dequantization of dY's rowwise copy (HBM-bound)
-        extras = {}
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         gemm_flops_one = 2.0 * TOKENS * FFN * HIDDEN
 
@@ -338,6 +377,9 @@ def main():
         extras["relative_rms_quantization_error"] = err
         return extras
 
+    if args.extras == "sweep":
+        print(json.dumps({"extras": {"quantizer_sweep": run_sweep()}}), flush=True)
+        return
     if args.extras == "only":
         step()
         torch.cuda.synchronize()

@@ -22,9 +22,6 @@ int set_hip_error(hipError_t e, const char* where) {
   return NVFP4_ERR_HIP;
 }
 
-// the tiled kernels put 128-row tiles on grid.y (at most 65535)
-constexpr int64_t kMaxTiledRows = INT64_C(65535) * 128;
-
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr int kMaxDevices = 64;
@@ -97,7 +94,6 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int rou
   if (rht != 0 && rht != 1) return NVFP4_ERR_ARG;
   if (codes_t && rht) return NVFP4_ERR_ARG;
   if (codes_t && rows % 16 != 0) return NVFP4_ERR_SHAPE;
-  if (codes_t && rows > kMaxTiledRows) return NVFP4_ERR_SHAPE;
   int cus = 0;
   if ((st = device_cus(&cus))) return st;
   nvfp4::QuantArgs a{x,      dtype == NVFP4_BF16, rows,   cols,   rounding,     seed,    rht == 1,
@@ -127,7 +123,7 @@ int nvfp4_quantize_2d(const void* w, int dtype, int64_t rows, int64_t cols, int 
                       uint8_t* scales_t, void* stream) {
   int st = validate_quant(w, dtype, rows, cols, rounding, codes, scales, tensor_scale, codes_t, scales_t);
   if (st) return st;
-  if (rows % 16 != 0 || rows > kMaxTiledRows) return NVFP4_ERR_SHAPE;
+  if (rows % 16 != 0) return NVFP4_ERR_SHAPE;
   int cus = 0;
   if ((st = device_cus(&cus))) return st;
   nvfp4::QuantArgs a{w,      dtype == NVFP4_BF16, rows, cols,   rounding,     seed,    false,

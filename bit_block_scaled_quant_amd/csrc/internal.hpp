@@ -42,7 +42,8 @@ struct CastTransposeArgs {
   float* tensor_scale;
   uint8_t* codes_t;
   uint8_t* scales_t;
-  float* tensor_scale_t;
+  float* tensor_scale_t;  // may equal tensor_scale when rht_t is off
+  uint32_t stream_t;      // SR stream of the columnwise copy: 0, or 1 for nvfp4_quantize's copy
 };
 
 void launch_cast_transpose(const CastTransposeArgs& a, int cus, hipStream_t st);

@@ -14,10 +14,9 @@
 // Pass 2 comes in three shapes:
 //   k_encode_rows   1x16 blocks along rows only: one thread per block,
 //                   coalesced 16-byte loads, 8-byte code stores;
-//   k_encode_tile1d 1x16 rowwise blocks plus the columnwise copy (blocks of
-//                   16 rows, written as rows of the transpose): a 128x128
-//                   tile is staged in LDS so that both copies leave in
-//                   coalesced 64-byte row segments;
+//   k_encode_ct     1x16 rowwise blocks plus the columnwise copy (blocks of
+//                   16 rows, written as rows of the transpose), described
+//                   with the cast-transpose below;
 //   k_encode_2d     16x16 blocks (2B.3): one wave per 16 x 64 strip, one
 //                   scale per block, each element encoded once and written
 //                   both ways, so the transposed copy is bit-identical to
@@ -33,7 +32,6 @@ namespace nvfp4 {
 
 constexpr int kThreads = 256;
 static_assert(kThreads >= kInvTable, "the inverse-scale table is built by one thread per entry");
-constexpr int kTile = 128;
 
 // codes of eight elements (element index0 .. index0 + 7, index0 % 8 == 0)
 template <bool SR>
@@ -231,114 +229,6 @@ __global__ __launch_bounds__(kThreads) void k_encode_rows_blk(const void* __rest
     reinterpret_cast<uint2*>(codes)[b] = encode16<SR>(v, inv, seed, 0u, (uint64_t)b * 16);
     scales[b] = (uint8_t)byte;
   }
-}
-
-// LDS tile element: the input's own storage type
-template <bool BF16>
-struct TileElem {
-  using T = float;
-  static constexpr int kPad = 4;
-  static __device__ __forceinline__ float to_float(T v) { return v; }
-};
-template <>
-struct TileElem<true> {
-  using T = uint16_t;
-  static constexpr int kPad = 8;
-  static __device__ __forceinline__ float to_float(T v) { return __uint_as_float((uint32_t)v << 16); }
-};
-
-// Load 16 input elements once: the raw storage goes to row segment `trow`
-// of the LDS tile, the fp32 values to v.
-template <bool BF16>
-__device__ __forceinline__ void load16_stash(const void* __restrict__ x, int64_t e,
-                                             typename TileElem<BF16>::T* trow, float v[16]) {
-  if (BF16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e);
-    const uint4 a = ld_stream(p), b = ld_stream(p + 1);
-    uint4* d = reinterpret_cast<uint4*>(trow);
-    d[0] = a;
-    d[1] = b;
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + e);
-    uint4* d = reinterpret_cast<uint4*>(trow);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 q = ld_stream(p + i);
-      d[i] = q;
-      v[4 * i] = __uint_as_float(q.x);
-      v[4 * i + 1] = __uint_as_float(q.y);
-      v[4 * i + 2] = __uint_as_float(q.z);
-      v[4 * i + 3] = __uint_as_float(q.w);
-    }
-  }
-}
-
-// Columnwise (transposed) 1D copy, one thread per (column, 64-row half):
-// blocks of 16 consecutive rows of a column, SR stream 1, element index of
-// the transposed tensor c * R + r.  Writes 8 bytes of codes per block.
-template <bool BF16, bool SR>
-__device__ __forceinline__ void columnwise_half(const typename TileElem<BF16>::T* tile, int pitch,
-                                                int col, int half, int rows_in, int64_t R,
-                                                int64_t r0, int64_t c, float s_enc,
-                                                const float* inv_tab, uint64_t seed,
-                                                uint8_t* __restrict__ codes_t,
-                                                uint8_t* __restrict__ scales_t) {
-#pragma unroll 1
-  for (int rb = half * 4; rb < half * 4 + 4; ++rb) {
-    if (rb * 16 >= rows_in) break;
-    float v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = TileElem<BF16>::to_float(tile[(rb * 16 + j) * pitch + col]);
-    float inv;
-    const uint32_t byte = block_scale(amax16(v), s_enc, inv_tab, &inv);
-    const int64_t r = r0 + rb * 16;
-    const uint2 q = encode16<SR>(v, inv, seed, 1u, (uint64_t)(c * R + r));
-    *reinterpret_cast<uint2*>(codes_t + c * (R / 2) + r / 2) = q;
-    scales_t[c * (R / 16) + r / 16] = (uint8_t)byte;
-  }
-}
-
-template <bool BF16, bool SR>
-__global__ __launch_bounds__(kThreads) void k_encode_tile1d(
-    const void* __restrict__ x, int64_t R, int64_t C, uint64_t seed, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t,
-    float* __restrict__ ts) {
-  using E = TileElem<BF16>;
-  constexpr int pitch = kTile + E::kPad;
-  __shared__ __align__(16) typename E::T tile[kTile * pitch];
-  __shared__ float inv_tab[kInvTable];
-
-  const float s_enc = tensor_scale_from_amax(ts[1]);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) ts[0] = s_enc;
-  build_inv_table(inv_tab, s_enc);
-  const int64_t r0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;
-  const int rows_in = (int)(R - r0 < kTile ? R - r0 : kTile);
-  const int cols_in = (int)(C - c0 < kTile ? C - c0 : kTile);
-
-  // rowwise blocks straight from registers; the raw values also go to LDS
-#pragma unroll 1
-  for (int q = threadIdx.x; q < kTile * (kTile / 16); q += kThreads) {
-    const int row = q >> 3, cb = q & 7;
-    if (row >= rows_in || cb * 16 >= cols_in) continue;
-    const int64_t e = (r0 + row) * C + c0 + cb * 16;
-    float v[16];
-    load16_stash<BF16>(x, e, tile + row * pitch + cb * 16, v);
-    float inv;
-    const uint32_t byte = block_scale(amax16(v), s_enc, inv_tab, &inv);
-    *reinterpret_cast<uint2*>(codes + e / 2) = encode16<SR>(v, inv, seed, 0u, (uint64_t)e);
-    scales[e / 16] = (uint8_t)byte;
-  }
-  __syncthreads();
-  const int col = threadIdx.x >> 1, half = threadIdx.x & 1;
-  if (col < cols_in)
-    columnwise_half<BF16, SR>(tile, pitch, col, half, rows_in, R, r0, c0 + col, s_enc, inv_tab, seed,
-                              codes_t, scales_t);
 }
 
 // 2D (16 x 16) blocks: one wave per strip of 16 rows x 64 columns (four
@@ -626,6 +516,19 @@ __device__ __forceinline__ void chunk_signs(Chunk16<BF16>& ch, uint32_t mask) {
   }
 }
 
+// An empty asm statement that claims to change every register of the chunk:
+// the second pass then extracts its fp32 values afresh.  Without it the
+// compiler keeps the 128 values the first pass extracted alive for reuse,
+// which does not fit in 128 VGPRs and spills.
+template <bool BF16>
+__device__ __forceinline__ void chunk_opaque(Chunk16<BF16>& ch) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int h = 0; h < (BF16 ? 1 : 2); ++h)
+      asm volatile("" : "+v"(ch.w[j][h].x), "+v"(ch.w[j][h].y), "+v"(ch.w[j][h].z), "+v"(ch.w[j][h].w));
+}
+
 // element (row j, column k of the lane) as fp32; j and k are compile-time
 template <bool BF16>
 __device__ __forceinline__ float chunk_elem(const Chunk16<BF16>& ch, int j, int k) {
@@ -712,7 +615,8 @@ __global__ __launch_bounds__(kThreads) void k_amax_ct(const void* __restrict__ x
 // 30% slower).
 template <bool BF16, bool SR, bool RHT>
 __global__ __launch_bounds__(kCtThreads, 4) void k_encode_ct(
-    const void* __restrict__ x, int64_t R, int64_t C, uint64_t seed, uint64_t seed_t, uint32_t rht_mask,
+    const void* __restrict__ x, int64_t R, int64_t C, uint64_t seed, uint64_t seed_t, uint32_t stream_t,
+    uint32_t rht_mask,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts,
     uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, float* __restrict__ ts_t) {
   // columnwise codes [chunk][column slot][8 bytes]: lane l's eight columns
@@ -771,9 +675,13 @@ __global__ __launch_bounds__(kCtThreads, 4) void k_encode_ct(
       if (lane_ok) *reinterpret_cast<uint32_t*>(codes + e / 2) = q;
       if (!odd) rs[16 * wv + j][lane >> 1] = (uint8_t)byte;
     }
-    // columnwise copy: the rows of x^T, SR stream 0 of seed_t, element index
-    // c * R + r (the index in x^T)
-    if (RHT) chunk_signs<BF16>(ch, rht_mask);
+    // columnwise copy: the rows of x^T, SR stream stream_t of seed_t (0 for
+    // the cast-transpose, 1 for the columnwise copy of one 1D quantization),
+    // element index c * R + r (the index in x^T)
+    if (RHT)
+      chunk_signs<BF16>(ch, rht_mask);
+    else
+      chunk_opaque<BF16>(ch);
     uint32_t sc_lo = 0u, sc_hi = 0u;
     uint8_t* tqw = tq + wv * kPitch + 64 * lane;
 #pragma unroll
@@ -785,7 +693,7 @@ __global__ __launch_bounds__(kCtThreads, 4) void k_encode_ct(
       float inv;
       const uint32_t byte = block_scale(max_abs16(v), s_enc_t, inv_tab[1], &inv);
       const int64_t c = c0 + cl + k;
-      const uint2 q = encode16<SR>(v, inv, seed_t, 0u, (uint64_t)(c * R + r0));
+      const uint2 q = encode16<SR>(v, inv, seed_t, stream_t, (uint64_t)(c * R + r0));
       *reinterpret_cast<uint2*>(tqw + 8 * (k ^ (lane & 7))) = q;
       if (k < 4)
         sc_lo |= byte << (8 * k);
@@ -900,6 +808,9 @@ static void launch_rows(const QuantArgs& a, int cus, hipStream_t st) {
                        a.tensor_scale);
 }
 
+template <bool BF16, bool SR, bool RHT>
+static void launch_ct_encode(const CastTransposeArgs& a, int cus, hipStream_t st);
+
 template <bool BF16, bool SR>
 static void launch_tile(const QuantArgs& a, bool two_d, int cus, hipStream_t st) {
   if (two_d) {
@@ -915,9 +826,12 @@ static void launch_tile(const QuantArgs& a, bool two_d, int cus, hipStream_t st)
       hipLaunchKernelGGL((k_encode_2d<BF16, SR, false>), dim3(blocks), dim3(kThreads), 0, st, a.x, a.rows,
                          a.cols, a.seed, a.codes, a.scales, a.codes_t, a.scales_t, a.tensor_scale);
   } else {
-    const dim3 grid((unsigned)((a.cols + kTile - 1) / kTile), (unsigned)((a.rows + kTile - 1) / kTile));
-    hipLaunchKernelGGL((k_encode_tile1d<BF16, SR>), grid, dim3(kThreads), 0, st, a.x, a.rows, a.cols,
-                       a.seed, a.codes, a.scales, a.codes_t, a.scales_t, a.tensor_scale);
+    // 1D with the columnwise copy: the cast-transpose encoder with one tensor
+    // scale for both copies and the columnwise SR draws from stream 1 of seed
+    CastTransposeArgs c{a.x,     a.bf16,   a.rows,         a.cols,  a.rounding, a.seed, a.seed,
+                        false,   0u,       a.codes,        a.scales, a.tensor_scale, a.codes_t, a.scales_t,
+                        a.tensor_scale, 1u};
+    launch_ct_encode<BF16, SR, false>(c, cus, st);
   }
 }
 
@@ -957,12 +871,12 @@ void launch_quantize(const QuantArgs& a, int cus, hipStream_t st) {
 }
 
 template <bool BF16, bool SR, bool RHT>
-static void launch_ct_encode(const CastTransposeArgs& a, hipStream_t st) {
+static void launch_ct_encode(const CastTransposeArgs& a, int, hipStream_t st) {
   const int64_t tiles = ((a.rows + 127) / 128) * ((a.cols + kCtCols - 1) / kCtCols);
   const int blocks = (int)(((tiles + 7) / 8) * 8);  // tiles <= 2^24 (rows * cols <= 2^40)
   hipLaunchKernelGGL((k_encode_ct<BF16, SR, RHT>), dim3(blocks), dim3(kCtThreads), 0, st, a.x, a.rows, a.cols,
-                     a.seed, a.seed_t, a.rht_mask, a.codes, a.scales, a.tensor_scale, a.codes_t, a.scales_t,
-                     a.tensor_scale_t);
+                     a.seed, a.seed_t, a.stream_t, a.rht_mask, a.codes, a.scales, a.tensor_scale, a.codes_t,
+                     a.scales_t, a.tensor_scale_t);
 }
 
 template <bool BF16>
@@ -976,18 +890,18 @@ static void launch_cast_transpose_t(const CastTransposeArgs& a, int cus, hipStre
     hipLaunchKernelGGL(k_amax_ct<BF16>, dim3(blocks), dim3(kThreads), 0, st, a.x, a.rows, a.cols, a.rht_mask,
                        a.tensor_scale, a.tensor_scale_t);
     if (sr)
-      launch_ct_encode<BF16, true, true>(a, st);
+      launch_ct_encode<BF16, true, true>(a, cus, st);
     else
-      launch_ct_encode<BF16, false, true>(a, st);
+      launch_ct_encode<BF16, false, true>(a, cus, st);
   } else {
     hipLaunchKernelGGL(k_init_amax, dim3(1), dim3(1), 0, st, a.tensor_scale);
     const int64_t nvec = a.rows * a.cols / (BF16 ? 8 : 4);
     hipLaunchKernelGGL((k_amax_plain<BF16>), dim3(grid_stride_blocks(nvec / 4, cus, 2)), dim3(kThreads), 0, st,
                        reinterpret_cast<const uint4*>(a.x), nvec, a.tensor_scale);
     if (sr)
-      launch_ct_encode<BF16, true, false>(a, st);
+      launch_ct_encode<BF16, true, false>(a, cus, st);
     else
-      launch_ct_encode<BF16, false, false>(a, st);
+      launch_ct_encode<BF16, false, false>(a, cus, st);
   }
 }
 

@@ -59,7 +59,7 @@ def test_quantize_rowwise(shape, dtype, rounding):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("rounding", [0, 1])
-@pytest.mark.parametrize("shape", SMALL)
+@pytest.mark.parametrize("shape", SMALL + [(400, 1040), (272, 1552)])
 def test_quantize_columnwise(shape, dtype, rounding):
     x = make(*shape, dtype, seed=shape[1], kind="act")
     q = nv.quantize(x.to(DEV), rounding=rounding, seed=5, transposed=True)
