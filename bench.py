@@ -363,6 +363,23 @@ def main():
                                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         del Wt, dYt_m, Xt_m, mxq, qa
 
+        # context, not part of the path: the vendor library's plain fp16 and
+        # bf16 GEMM (torch.matmul -> hipBLASLt) on the same three shapes, with
+        # already-dequantized 16-bit operands and a 16-bit output (no unpack,
+        # half the output bytes of the fp32 C above)
+        lib = {}
+        for name, (M, N, K) in (("fprop", (TOKENS, FFN, HIDDEN)), ("dgrad", (TOKENS, HIDDEN, FFN)),
+                                ("wgrad", (FFN, HIDDEN, TOKENS))):
+            for dt, tag in ((torch.float16, "fp16"), (torch.bfloat16, "bf16")):
+                a16 = torch.randn(M, K, device=dev, dtype=dt)
+                b16 = torch.randn(N, K, device=dev, dtype=dt)
+                c16 = torch.empty(M, N, device=dev, dtype=dt)
+                ms = timed_ms(lambda: torch.matmul(a16, b16.t(), out=c16))
+                lib[f"{name}_{tag}"] = {"ms": round(ms, 4),
+                                        "TFLOP/s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+                del a16, b16, c16
+        extras["library_gemm_16bit_reference"] = lib
+
         def rel_err(t, deq):
             d = (deq.double() - t.double())
             return float(torch.linalg.vector_norm(d) / torch.linalg.vector_norm(t.double()))
