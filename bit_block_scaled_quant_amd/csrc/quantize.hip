@@ -571,30 +571,80 @@ __global__ void k_init_amax2(float* ts, float* ts_t) {
 // Pass 1 with the transform: the plain amax (rowwise copy) and the amax
 // after the transform of every 16-row column block (columnwise copy) from
 // one read.  |sigma x| = |x|, so the plain amax is taken after the flips.
+//
+// A wave takes chunks of 16 rows x 256 columns: lane l holds columns
+// 4l .. 4l + 3 of the 16 rows (one 8-byte load per row for bf16, so a load
+// instruction reads 512 contiguous bytes), i.e. four whole column blocks.
+// Waves walk the chunks grid-stride with the next chunk's loads in flight
+// while the current one is transformed.  A lane past the last column reads
+// the last four columns instead: a duplicate cannot change a maximum, and
+// every lane then loads without a branch.
+constexpr int kAmaxCtCols = 256;
+
+template <bool BF16>
+struct Col4 {
+  uint32_t w[16][BF16 ? 2 : 4];  // row j: the lane's four columns
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_col4(const void* __restrict__ x, int64_t e0, int64_t C, Col4<BF16>& c) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (BF16) {
+      typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+      const u32x2_t v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(x) + e0 + j * C));
+      c.w[j][0] = v.x;
+      c.w[j][1] = v.y;
+    } else {
+      const uint4 v = ld_stream(static_cast<const float*>(x) + e0 + j * C);
+      c.w[j][0] = v.x;
+      c.w[j][1] = v.y;
+      c.w[j][2] = v.z;
+      c.w[j][3] = v.w;
+    }
+  }
+}
+
+// element (row j, column k of the lane) with sign j of the transform
+template <bool BF16>
+__device__ __forceinline__ float col4_elem(const Col4<BF16>& c, int j, int k, uint32_t mask) {
+  const uint32_t w = c.w[j][BF16 ? (k >> 1) : k];
+  const uint32_t b = BF16 ? ((k & 1) ? (w & 0xFFFF0000u) : (w << 16)) : w;
+  return __uint_as_float(b ^ (((mask >> j) & 1u) << 31));
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_amax_ct(const void* __restrict__ x, int64_t R, int64_t C,
                                                       uint32_t rht_mask, float* __restrict__ ts,
                                                       float* __restrict__ ts_t) {
   const int lane = threadIdx.x & 63;
-  const int64_t cchunks = (C + kCtCols - 1) / kCtCols;
+  const int64_t cchunks = (C + kAmaxCtCols - 1) / kAmaxCtCols;
   const int64_t nchunks = (R / 16) * cchunks;
   const int64_t wstride = (int64_t)gridDim.x * (kThreads / 64);
+  // first element of the lane's columns in chunk q (clamped to the last
+  // four columns of the tensor; C % 16 == 0)
+  auto elem0 = [&](int64_t q) {
+    const int64_t col = min<int64_t>((q % cchunks) * kAmaxCtCols + 4 * lane, C - 4);
+    return (q / cchunks) * 16 * C + col;
+  };
   float m = 0.0f, mt = 0.0f;
-  for (int64_t q = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); q < nchunks; q += wstride) {
-    const int64_t col = (q % cchunks) * kCtCols + 8 * lane;
-    if (col >= C) continue;  // C % 16 == 0: a lane has all eight columns or none
-    Chunk16<BF16> ch;
-    load_chunk<BF16>(x, (q / cchunks) * 16 * C + col, C, ch);
-    chunk_signs<BF16>(ch, rht_mask);
+  int64_t q = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  Col4<BF16> cur, nxt;
+  if (q < nchunks) load_col4<BF16>(x, elem0(q), C, cur);
+  for (; q < nchunks; q += wstride) {
+    const bool more = q + wstride < nchunks;  // wave-uniform
+    if (more) load_col4<BF16>(x, elem0(q + wstride), C, nxt);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       float v[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = chunk_elem<BF16>(ch, j, k);
+      for (int j = 0; j < 16; ++j) v[j] = col4_elem<BF16>(cur, j, k, rht_mask);
       m = fmaxf(m, max_abs16(v));
       hadamard16<false>(v);
       mt = fmaxf(mt, max_abs16(v));
     }
+    if (more) cur = nxt;
   }
   // the transform's final 1/4, applied to the maximum (rounding is monotone)
   block_max2_to(m, 0.25f * mt, ts, ts_t);
@@ -884,9 +934,10 @@ static void launch_cast_transpose_t(const CastTransposeArgs& a, int cus, hipStre
   const bool sr = a.rounding == 1;
   if (a.rht_t) {
     hipLaunchKernelGGL(k_init_amax2, dim3(1), dim3(1), 0, st, a.tensor_scale, a.tensor_scale_t);
-    const int64_t nchunks = (a.rows / 16) * ((a.cols + kCtCols - 1) / kCtCols);
+    // four workgroups of four waves per CU, each wave walking several chunks
+    const int64_t nchunks = (a.rows / 16) * ((a.cols + kAmaxCtCols - 1) / kAmaxCtCols);
     const int blocks = (int)std::max<int64_t>(
-        1, std::min<int64_t>((nchunks + kThreads / 64 - 1) / (kThreads / 64), (int64_t)cus * 32));
+        1, std::min<int64_t>((nchunks + kThreads / 64 - 1) / (kThreads / 64), (int64_t)cus * 4));
     hipLaunchKernelGGL(k_amax_ct<BF16>, dim3(blocks), dim3(kThreads), 0, st, a.x, a.rows, a.cols, a.rht_mask,
                        a.tensor_scale, a.tensor_scale_t);
     if (sr)
