@@ -667,8 +667,10 @@ template <bool BF16, bool SR, bool RHT>
 __global__ __launch_bounds__(kCtThreads, 4) void k_encode_ct(
     const void* __restrict__ x, int64_t R, int64_t C, uint64_t seed, uint64_t seed_t, uint32_t stream_t,
     uint32_t rht_mask,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts,
-    uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, float* __restrict__ ts_t) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* ts, uint8_t* __restrict__ codes_t,
+    uint8_t* __restrict__ scales_t, float* ts_t) {
+  // (ts and ts_t are the same two floats when the columnwise copy shares the
+  // rowwise tensor scale, so they are not restrict)
   // columnwise codes [chunk][column slot][8 bytes]: lane l's eight columns
   // fill bytes 64l .. 64l + 63 of a chunk row, column 8l + k in slot
   // k ^ (l & 7) (the xor spreads a store instruction over the banks); 16
