@@ -48,7 +48,6 @@ __global__ __launch_bounds__(kDqThreads) void k_dequantize(const uint8_t* __rest
     }
     // streaming stores: the output is written once and not read here
     if (BF16OUT) {
-      typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
       const u32x2_t w = {bf16_rne(v[0]) | bf16_rne(v[1]) << 16, bf16_rne(v[2]) | bf16_rne(v[3]) << 16};
       __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + 4 * q));
     } else {

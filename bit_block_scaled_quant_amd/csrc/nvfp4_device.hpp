@@ -229,6 +229,13 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// the same for 8 bytes
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld_stream8(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
 // 16 consecutive elements starting at element e (e % 16 == 0) as fp32
 template <bool BF16>
 __device__ __forceinline__ void load16(const void* __restrict__ x, int64_t e, float v[16]) {

@@ -591,9 +591,7 @@ __device__ __forceinline__ void load_col4(const void* __restrict__ x, int64_t e0
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (BF16) {
-      typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-      const u32x2_t v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(x) + e0 + j * C));
+      const uint2 v = ld_stream8(static_cast<const uint16_t*>(x) + e0 + j * C);
       c.w[j][0] = v.x;
       c.w[j][1] = v.y;
     } else {
