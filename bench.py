@@ -70,6 +70,14 @@ def quant_bytes(rows, cols, in_bytes, transposed):
     return 2 * in_bytes * n + copies * n * (0.5 + 1.0 / 16.0)
 
 
+def qmeta(rows, cols, in_bytes, transposed):
+    """Bytes of one quantize call: the algorithmic bytes (two reads of the
+    input, the method's amax pass then its encode pass) and the single-read
+    lower bound (one read of the input), both with every output written."""
+    alg = quant_bytes(rows, cols, in_bytes, transposed)
+    return {"alg": alg, "one_read": alg - in_bytes * rows * cols}
+
+
 def gemm_bytes(M, N, K):
     return (M + N) * K * (0.5 + 1.0 / 16.0) + 4.0 * M * N
 
@@ -195,7 +203,7 @@ def main():
 
     quant_W = ("quant_W_2d_rne_t", "quant", lambda: nv.nvfp4_quantize_2d(
         W, 0, 0, qW.codes, qW.scales, qW.tensor_scale, qW.codes_t, qW.scales_t),
-        quant_bytes(FFN, HIDDEN, 2, True))
+        qmeta(FFN, HIDDEN, 2, True))
     gemm_fprop = ("gemm_fprop", "gemm", lambda: nv.gemm(qX, qW, out=Y), (TOKENS, FFN, HIDDEN))
     gemm_dgrad = ("gemm_dgrad", "gemm", lambda: nv.gemm(qdY, qWt, out=dX), (TOKENS, HIDDEN, FFN))
     gemm_wgrad = ("gemm_wgrad", "gemm", lambda: nv.gemm(qdYt, qXt, out=dW), (FFN, HIDDEN, TOKENS))
@@ -203,18 +211,18 @@ def main():
         calls = [
             ("quant_X_1d_rne", "quant", lambda: nv.nvfp4_quantize(X, 0, 0, 0, 0, qX.codes, qX.scales,
                                                                   qX.tensor_scale),
-             quant_bytes(TOKENS, HIDDEN, 2, False)),
+             qmeta(TOKENS, HIDDEN, 2, False)),
             quant_W, gemm_fprop,
             ("quant_dY_1d_sr", "quant", lambda: nv.nvfp4_quantize(dY, 1, seed, 0, 0, qdY.codes,
                                                                   qdY.scales, qdY.tensor_scale),
-             quant_bytes(TOKENS, FFN, 2, False)),
+             qmeta(TOKENS, FFN, 2, False)),
             gemm_dgrad,
             ("quant_dYt_1d_sr_rht", "quant", lambda: nv.nvfp4_quantize(
                 dYt, 1, seed, 1, seed, qdYt.codes, qdYt.scales, qdYt.tensor_scale),
-             quant_bytes(FFN, TOKENS, 2, False)),
+             qmeta(FFN, TOKENS, 2, False)),
             ("quant_Xt_1d_rne_rht", "quant", lambda: nv.nvfp4_quantize(
                 Xt, 0, 0, 1, seed, qXt.codes, qXt.scales, qXt.tensor_scale),
-             quant_bytes(HIDDEN, TOKENS, 2, False)),
+             qmeta(HIDDEN, TOKENS, 2, False)),
             gemm_wgrad,
         ]
     else:
@@ -222,11 +230,11 @@ def main():
         calls = [
             ("ct_X_rne_rht", "quant", lambda: nv.nvfp4_quantize_cast_transpose(
                 X, 0, 0, 0, 1, seed, qX.codes, qX.scales, qX.tensor_scale, qXt.codes, qXt.scales,
-                qXt.tensor_scale), quant_bytes(TOKENS, HIDDEN, 2, True)),
+                qXt.tensor_scale), qmeta(TOKENS, HIDDEN, 2, True)),
             quant_W, gemm_fprop,
             ("ct_dY_sr_rht", "quant", lambda: nv.nvfp4_quantize_cast_transpose(
                 dY, 1, seed, seed, 1, seed, qdY.codes, qdY.scales, qdY.tensor_scale, qdYt.codes,
-                qdYt.scales, qdYt.tensor_scale), quant_bytes(TOKENS, FFN, 2, True)),
+                qdYt.scales, qdYt.tensor_scale), qmeta(TOKENS, FFN, 2, True)),
             gemm_dgrad, gemm_wgrad,
         ]
 
@@ -269,10 +277,13 @@ def main():
                         torch.cuda.synchronize()
                         ts.append(a.elapsed_time(b))
                     ms = float(np.median(ts))
-                    gbs = quant_bytes(rows, cols, 2, True) / (ms * 1e-3) / 1e9
+                    qm = qmeta(rows, cols, 2, True)
+                    gbs = qm["alg"] / (ms * 1e-3) / 1e9
                     key = f"{rows}x{cols}_{'2d' if two_d else '1d'}+t_{'sr' if rnd else 'rne'}"
                     res[key] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
-                                "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+                                "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                "frac_hbm_peak_one_read_bound": round(
+                                    qm["one_read"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             del xs, qs
         del flush
         return res
@@ -463,11 +474,15 @@ def main():
             components[name] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
                                 "frac_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
         else:
-            gbs = meta / (ms * 1e-3) / 1e9
+            gbs = meta["alg"] / (ms * 1e-3) / 1e9
             quant_ms_total += ms
-            quant_bytes_total += meta
+            quant_bytes_total += meta["alg"]
+            # frac_hbm_peak_one_read_bound: the same time against the bytes of a
+            # single read of the input (what a known amax would allow)
             components[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
-                                "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+                                "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                "frac_hbm_peak_one_read_bound": round(
+                                    meta["one_read"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
     avg_gemm_ms = float(np.mean(gemm_ms))
     achieved = gemm_flops / (avg_gemm_ms * 1e-3) / 1e12
