@@ -310,8 +310,12 @@ __global__ __launch_bounds__(kThreads) void k_encode_2d(
   const int64_t tiles_c = (C + 4 * kStripCols - 1) / (4 * kStripCols);
   const int64_t ntiles = ((R + 127) / 128) * tiles_c;
   // Workgroups are dealt to the eight XCDs in turn; tile numbers are laid
-  // out so that each XCD takes a contiguous run of tiles in row-major order,
-  // and output lines shared by neighbouring tiles are completed in one L2.
+  // out so that each XCD takes a contiguous run of tiles in column-major
+  // order: the tiles that complete one line of the transposed codes (64
+  // bytes each) and of the transposed scales (8 bytes each) are then
+  // neighbours in one L2 (column-major instead of row-major: W's writes
+  // 143.6 -> 126.9 MB for 118 MB of output, the cold-cache 2D calls 3-6%
+  // faster).
   const int64_t per_xcd = (ntiles + 7) / 8;
   const int64_t tile = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (tile >= ntiles) return;
@@ -323,9 +327,10 @@ __global__ __launch_bounds__(kThreads) void k_encode_2d(
   const int rh = (lane >> 3) & 1, ch = (lane >> 2) & 1, jq = lane & 3;
   // a workgroup tile is 128 rows x 256 columns; wave wv walks down its
   // 64-column strip
-  const int64_t tc0 = (tile % tiles_c) * (4 * kStripCols);
+  const int64_t tiles_r = (R + 127) / 128;
+  const int64_t tc0 = (tile / tiles_r) * (4 * kStripCols);
   const int64_t c0 = tc0 + wv * kStripCols;
-  const int64_t rt = (tile / tiles_c) * 128;
+  const int64_t rt = (tile % tiles_r) * 128;
   if (!STAGED && c0 >= C) return;
   const int64_t col = c0 + 8 * c;
   const bool act = STAGED || col < C;  // C % 16 == 0: both halves of a block agree
