@@ -602,18 +602,44 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_
   // 8 * (k / 4) + 4 * (l / 32) + k % 4
   const float inv_a = __fdiv_rn(1.0f, g.a_ts[0]), inv_b = __fdiv_rn(1.0f, g.b_ts[0]);
   float cmax = 0.0f;
+  if (EX && g.c16 && g.beta == 0.0f && ((uintptr_t)g.c16 & 3) == 0) {
+    // bf16 output without beta: columns n and n + 1 sit in lanes r and r ^ 1,
+    // and values k, k + 1 (k even) in rows m, m + 1.  The lane pair swaps one
+    // value, so the even lane stores row m and the odd lane row m + 1 as two
+    // bf16 in 4 bytes each (half the store instructions of one bf16 per lane)
+    const bool odd = r & 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int64_t n = n0 + wn * 32 * NT + j * 32 + r;
+      for (int j = 0; j < NT; ++j) {
+        const int64_t n = n0 + wn * 32 * NT + j * 32 + (r & ~1);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (k >> 2) + 4 * gq + (k & 3);
-        if (EX)
-          store_c(g, m * g.N + n, (acc[i][j][k] * inv_a) * inv_b, cmax, true);
-        else  // streaming store: C is written once and not read here (+2.5% measured)
-          __builtin_nontemporal_store((acc[i][j][k] * inv_a) * inv_b, &g.c[m * g.N + n]);
+        for (int k = 0; k < 16; k += 2) {
+          const int64_t m = m0 + wm * 128 + i * 32 + 8 * (k >> 2) + 4 * gq + (k & 3);
+          const uint32_t h0 = bf16_rne((acc[i][j][k] * inv_a) * inv_b);
+          const uint32_t h1 = bf16_rne((acc[i][j][k + 1] * inv_a) * inv_b);
+          cmax = fmaxf(cmax, fmaxf(fabsf(__uint_as_float(h0 << 16)), fabsf(__uint_as_float(h1 << 16))));
+          const uint32_t other =
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? h0 : h1), 0xB1, 0xF, 0xF, true);
+          const uint32_t packed = odd ? (other | (h1 << 16)) : (h0 | (other << 16));
+          __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t*>(g.c16 + (odd ? m + 1 : m) * g.N + n));
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int64_t n = n0 + wn * 32 * NT + j * 32 + r;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int64_t m = m0 + wm * 128 + i * 32 + 8 * (k >> 2) + 4 * gq + (k & 3);
+          if (EX)
+            store_c(g, m * g.N + n, (acc[i][j][k] * inv_a) * inv_b, cmax, true);
+          else  // streaming store: C is written once and not read here (+2.5% measured)
+            __builtin_nontemporal_store((acc[i][j][k] * inv_a) * inv_b, &g.c[m * g.N + n]);
+        }
       }
     }
   }

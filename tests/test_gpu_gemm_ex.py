@@ -56,6 +56,38 @@ def test_gemm_ex(M, N, K, dtype, beta):
     assert amax.item() == float(np.abs(c.float().cpu().numpy()).max())
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("beta", [0.0, 0.5])
+def test_gemm_ex_whole_waves(dtype, beta):
+    # 256 tiles of 256 x 256: the whole-wave kernel (the shapes above run as
+    # 256 x 128 halves); sampled outputs against the oracle, the amax exactly
+    M, N, K = 4096, 4096, 512
+    ah = datagen.host_input(datagen.act(tokens=M, hidden=K, seed=21))
+    bh = datagen.host_input(datagen.weight(out_features=N, in_features=K, seed=22))
+    qa, qb = oracle.quantize_1d(ah), oracle.quantize_1d(bh)
+    up = lambda q: nv.Quantized(torch.from_numpy(q[0]).to(DEV), torch.from_numpy(q[1]).to(DEV),
+                                torch.from_numpy(q[2]).to(DEV))
+    rng = np.random.default_rng(5)
+    ii = np.concatenate([[0, M - 1, 0, M - 1], rng.integers(0, M, 3000)]).astype(np.int64)
+    jj = np.concatenate([[0, 0, N - 1, N - 1], rng.integers(0, N, 3000)]).astype(np.int64)
+    ref, absum = oracle.gemm_sample(qa[0], qa[1], qa[2][0], qb[0], qb[1], qb[2][0], ii, jj)
+    g = torch.Generator().manual_seed(4)
+    c_in = (torch.randn(M, N, generator=g) * float(np.abs(ref).max())).to(dtype)
+    c = c_in.to(DEV)
+    amax = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    nv.gemm_ex(up(qa), up(qb), out=c, beta=beta, amax=amax)
+    torch.cuda.synchronize()
+    got = c.float().cpu().numpy()[ii, jj].astype(np.float64)
+    cin = c_in.float().numpy()[ii, jj].astype(np.float64)
+    want = ref + beta * cin
+    bound = 1e-5 * absum + 2.0 ** -22 * (np.abs(ref) + np.abs(beta * cin))
+    if dtype == torch.bfloat16:
+        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(want)
+    excess = np.abs(got - want) - bound
+    assert excess.max() <= 0, f"max excess {excess.max()} at sample {excess.argmax()}"
+    assert amax.item() == float(c.float().abs().max().item())
+
+
 @pytest.mark.parametrize("rounding,rht", [(0, 0), (1, 0), (1, 1)])
 def test_quantize_with_amax_equals_oracle(rounding, rht):
     x = datagen.grad(tokens=304, out_features=1024, seed=7)
