@@ -158,7 +158,9 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
  * a_tensor_scale[0]) and B one of N x K, both quantized along K.  Tensor
  * scales are read on the device (the outputs of the quantizers), so no host
  * synchronization is needed.  Any result within
- * 1e-5 * sum_k |deq(A)_ik deq(B)_jk| of the exact sum is correct.
+ * 1e-5 * sum_k |deq(A)_ik deq(B)_jk| of the exact sum is correct.  Scale
+ * bytes are those the quantizers produce (0x00 .. 0x7E); the kernels read
+ * the low seven bits of a byte.
  * Shapes: M, N >= 1, K >= 16, K % 16 == 0.  Alignment: codes 8 bytes, C 4
  * bytes (16-byte codes, 8-byte scales and K % 128 == 0 take the fast path).
  */
