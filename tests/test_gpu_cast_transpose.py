@@ -39,7 +39,7 @@ def oracle_pair(xh, rounding, seed, seed_t, rht_t, rht_seed):
 
 
 SMALL = [(16, 16), (48, 80), (128, 512), (160, 272), (304, 1040), (144, 528), (256, 4096),
-         (1024, 1536)]
+         (1024, 1536), (4096, 16), (16, 8192)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -59,7 +59,7 @@ def test_quantize_rowwise(shape, dtype, rounding):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("rounding", [0, 1])
-@pytest.mark.parametrize("shape", SMALL + [(400, 1040), (272, 1552)])
+@pytest.mark.parametrize("shape", SMALL + [(400, 1040), (272, 1552), (4096, 16), (16, 8192)])
 def test_quantize_columnwise(shape, dtype, rounding):
     x = make(*shape, dtype, seed=shape[1], kind="act")
     q = nv.quantize(x.to(DEV), rounding=rounding, seed=5, transposed=True)
@@ -70,7 +70,7 @@ def test_quantize_columnwise(shape, dtype, rounding):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("rounding", [0, 1])
-@pytest.mark.parametrize("shape", SMALL + [(400, 48), (384, 512)])
+@pytest.mark.parametrize("shape", SMALL + [(400, 48), (384, 512), (4096, 16), (16, 8192)])
 def test_quantize_2d(shape, dtype, rounding):
     w = datagen.weight(out_features=shape[0], in_features=shape[1], seed=shape[0] + shape[1])
     w = w.float() if dtype == "f32" else w
