@@ -288,9 +288,28 @@ def main():
         del flush
         return res
 
+    def copy_bandwidth(reps=10):
+        """A plain 1 GiB device-to-device copy (torch's copy kernel): the HBM
+        rate a streaming kernel reaches on this machine, beside the 8 TB/s
+        datasheet peak the fractions use.  Bytes = read + write."""
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        gbs = 2 * src.numel() * 4 / (ms * 1e-3) / 1e9
+        del src, dst
+        return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
     def run_extras():
         """Measurements outside the step (not part of value)."""
-        extras = {"quantizer_sweep": run_sweep()}
+        extras = {"copy_1GiB": copy_bandwidth(), "quantizer_sweep": run_sweep()}
         # outside the step: dequantization of dY's rowwise copy (HBM-bound)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         gemm_flops_one = 2.0 * TOKENS * FFN * HIDDEN
@@ -406,7 +425,8 @@ def main():
         return extras
 
     if args.extras == "sweep":
-        print(json.dumps({"extras": {"quantizer_sweep": run_sweep()}}), flush=True)
+        print(json.dumps({"extras": {"copy_1GiB": copy_bandwidth(), "quantizer_sweep": run_sweep()}}),
+              flush=True)
         return
     if args.extras == "only":
         step()
