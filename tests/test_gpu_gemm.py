@@ -100,11 +100,18 @@ def sample_positions(M, N, n=3000, seed=0):
         jj += [int(rng.integers(0, N)), int(rng.integers(0, N)), t % N, (N - 1 - t) % N]
     ii += list(rng.integers(0, M, n))
     jj += list(rng.integers(0, N, n))
+    # one output in every 256 x 128 block (a whole tile is two, a half tile one)
+    for bm in range(0, M, 256):
+        for bn in range(0, N, 128):
+            ii.append(bm + int(rng.integers(0, min(256, M - bm))))
+            jj.append(bn + int(rng.integers(0, min(128, N - bn))))
     return np.array(ii, np.int64), np.array(jj, np.int64)
 
 
 def gemm_full_case(a_ref, b_ref, M, N, K):
-    c = nv.gemm(upload(a_ref), upload(b_ref))
+    # C starts as NaN, so the finiteness check below also shows every output was written
+    c = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    nv.gemm(upload(a_ref), upload(b_ref), out=c)
     torch.cuda.synchronize()
     ii, jj = sample_positions(M, N)
     ref, refabs = oracle.gemm_sample(a_ref[0], a_ref[1], a_ref[2][0], b_ref[0], b_ref[1],
@@ -138,3 +145,35 @@ def test_gemm_full_wgrad():
     xt = datagen.act(DEV).t().contiguous()
     gemm_full_case(oracle.quantize_1d(datagen.bf16_bits(dyt), rounding=1, rht=1),
                    oracle.quantize_1d(datagen.bf16_bits(xt), rht=1), 20480, 5120, 8192)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M,N", [(8448, 2816), (4096, 4352)])
+def test_gemm_ragged_tile_counts(M, N):
+    # 363 tiles (XCD runs of unequal length, idle workgroups in the last one)
+    # and 272 tiles (a last wave of 256 x 128 halves); sampled outputs against
+    # the oracle, every output written
+    K = 512
+    a = datagen.host_input(datagen.act(tokens=M, hidden=K, seed=M))
+    b = datagen.host_input(datagen.weight(out_features=N, in_features=K, seed=N))
+    gemm_full_case(oracle.quantize_1d(a), oracle.quantize_1d(b, rounding=1, seed=2), M, N, K)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M,N,K", [(8192, 20480, 5120), (8192, 5120, 20480), (20480, 5120, 8192),
+                                   (8448, 2816, 512)])
+def test_gemm_plain_and_ex_epilogues_agree(M, N, K):
+    # nvfp4_gemm and nvfp4_gemm_ex (fp32 out, beta 0, with an amax target)
+    # run the same MFMA sequence per output with different epilogue code:
+    # the outputs must agree bit for bit everywhere, and the amax is max |C|
+    a = nv.quantize(datagen.act(tokens=M, hidden=K, seed=1).to(DEV))
+    b = nv.quantize(datagen.weight(out_features=N, in_features=K, seed=2).to(DEV), rounding=1, seed=3)
+    c1 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    nv.gemm(a, b, out=c1)
+    c2 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    amax = torch.zeros(1, dtype=torch.float32, device=DEV)
+    nv.gemm_ex(a, b, out=c2, amax=amax)
+    torch.cuda.synchronize()
+    assert torch.isfinite(c1).all()
+    assert torch.equal(c1, c2)
+    assert amax.item() == c1.abs().max().item()
