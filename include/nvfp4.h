@@ -158,7 +158,11 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
  * a_tensor_scale[0]) and B one of N x K, both quantized along K.  Tensor
  * scales are read on the device (the outputs of the quantizers), so no host
  * synchronization is needed.  Any result within
- * 1e-5 * sum_k |deq(A)_ik deq(B)_jk| of the exact sum is correct.  Scale
+ * 1e-5 * sum_k |deq(A)_ik deq(B)_jk| of the exact sum is correct.  The
+ * kernels accumulate code * scale products and then apply the tensor scales
+ * in fp32 as (acc * (1 / S_A)) * (1 / S_B), so the bound holds while that
+ * sum, (acc / S_A) and the result stay within fp32's normal range (no
+ * underflow below 2^-126, no overflow).  Scale
  * bytes are those the quantizers produce (0x00 .. 0x7E); the kernels read
  * the low seven bits of a byte.
  * Shapes: M, N >= 1, K >= 16, K % 16 == 0.  Alignment: codes 8 bytes, C 4

@@ -78,6 +78,22 @@ def test_gemm_exact_with_unit_scales(M, N, K):
     assert np.array_equal(c.cpu().numpy().astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (100, 70, 96)])
+@pytest.mark.parametrize("sa,sb", [(1e-30, 1e30), (1e30, 1e-30)])
+def test_gemm_extreme_tensor_scales(M, N, K, sa, sb):
+    # tensor scales near 2.7e33 and 2.7e-27: the reciprocals are applied one
+    # after the other in fp32, and every intermediate stays a normal number
+    a = datagen.tiny(tag=datagen.TAG_A, rows=M, cols=K, seed=7) * sa
+    b = datagen.tiny(tag=datagen.TAG_B, rows=N, cols=K, seed=8) * sb
+    ra = oracle.quantize_1d(a.numpy())
+    rb = oracle.quantize_1d(b.numpy(), rounding=1, seed=4)
+    c = nv.gemm(upload(ra), upload(rb))
+    torch.cuda.synchronize()
+    ref, refabs = oracle.gemm(ra[0], ra[1], ra[2][0], rb[0], rb[1], rb[2][0])
+    assert np.abs(ref).max() > 1.0  # the product itself is of ordinary size
+    check_full(c, ref, refabs)
+
+
 def test_gemm_symmetry_and_determinism():
     a = datagen.tiny(tag=datagen.TAG_A, rows=192, cols=512, seed=5)
     b = datagen.tiny(tag=datagen.TAG_B, rows=320, cols=512, seed=6)
