@@ -98,7 +98,7 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int rou
   if ((st = device_cus(&cus))) return st;
   nvfp4::QuantArgs a{x,      dtype == NVFP4_BF16, rows,   cols,   rounding,     seed,    rht == 1,
                      rht ? nvfp4::rht_sign_mask(rht_seed) : 0u,  false, codes, scales, tensor_scale,
-                     codes_t, scales_t};
+                     codes_t, scales_t, false};
   nvfp4::launch_quantize(a, cus, (hipStream_t)stream);
   return check_launch("nvfp4_quantize");
 }
@@ -127,7 +127,7 @@ int nvfp4_quantize_2d(const void* w, int dtype, int64_t rows, int64_t cols, int 
   int cus = 0;
   if ((st = device_cus(&cus))) return st;
   nvfp4::QuantArgs a{w,      dtype == NVFP4_BF16, rows, cols,   rounding,     seed,    false,
-                     0u,     true,                codes, scales, tensor_scale, codes_t, scales_t};
+                     0u,     true,                codes, scales, tensor_scale, codes_t, scales_t, false};
   nvfp4::launch_quantize(a, cus, (hipStream_t)stream);
   return check_launch("nvfp4_quantize_2d");
 }
@@ -146,7 +146,7 @@ int nvfp4_quantize_cast_transpose(const void* x, int dtype, int64_t rows, int64_
   if ((st = device_cus(&cus))) return st;
   nvfp4::CastTransposeArgs a{x,      dtype == NVFP4_BF16, rows,   cols,         rounding, seed,     seed_t,
                              rht_t == 1, rht_t ? nvfp4::rht_sign_mask(rht_seed) : 0u, codes, scales,
-                             tensor_scale, codes_t, scales_t, tensor_scale_t};
+                             tensor_scale, codes_t, scales_t, tensor_scale_t, 0u};
   nvfp4::launch_cast_transpose(a, cus, (hipStream_t)stream);
   return check_launch("nvfp4_quantize_cast_transpose");
 }

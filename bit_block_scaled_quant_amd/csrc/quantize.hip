@@ -762,7 +762,7 @@ __global__ __launch_bounds__(kCtThreads, 4) void k_encode_ct(
   // rowwise scales: 32 bytes per row of the tile
   const int64_t srow = C / 16;
   if (ncols == kCtCols && srow % 16 == 0 && ((uintptr_t)scales & 15) == 0) {
-    if (threadIdx.x < 32 * nch) {
+    if ((int)threadIdx.x < 32 * nch) {
       const int row = threadIdx.x >> 1, p = threadIdx.x & 1;
       *reinterpret_cast<uint4*>(scales + (rt + row) * srow + c0 / 16 + 16 * p) =
           *reinterpret_cast<const uint4*>(&rs[row][16 * p]);
@@ -799,7 +799,7 @@ __global__ __launch_bounds__(kCtThreads, 4) void k_encode_ct(
   }
   // columnwise scales: one thread per column, one byte per chunk
   const int64_t spitch = R / 16;
-  if (threadIdx.x < ncols) {
+  if ((int)threadIdx.x < ncols) {
     const int cc = threadIdx.x;
     uint8_t* dst = scales_t + (c0 + cc) * spitch + rt / 16;
     if (nch == kCtChunks && spitch % 8 == 0 && ((uintptr_t)scales_t & 7) == 0) {
