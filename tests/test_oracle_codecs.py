@@ -11,6 +11,8 @@
 * E2M1 stochastic rounding: support {lo, hi}, exact threshold, and the worked
   example of "Pretraining Large Language Models with NVFP4" (lay part, "De
   Vier Slimme Trucs", the rounding of 3.4): P(3) = 0.6, P(4) = 0.4.
+* Dequantize: every (code, scale byte) pair under five tensor scales against
+  the bit-field E2M1 value times torch's E4M3 value, divided once in double.
 """
 import json
 import os
@@ -188,3 +190,23 @@ def test_e4m3_encode_random(orc):
     s = np.exp(rng.uniform(np.log(1e-45), np.log(464), size=3_000_000)).astype(np.float32)
     s = s[s <= 464]
     assert np.array_equal(orc.e4m3_encode_n(s), torch_e4m3(s))
+
+
+# ---------------------------------------------------------- dequantize ---
+@pytest.mark.parametrize("s_enc", [1.0, 2688.0 / 3.7, 3.4028234663852886e38, 7.899e-36, 0.3])
+def test_dequantize_every_code_and_scale_byte(orc, s_enc):
+    # "Pretraining Large Language Models with NVFP4", 2A: an element is its
+    # E2M1 code times its block's E4M3 scale, over the FP32 tensor scale.
+    # Independent route: E2M1 from its bit fields, E4M3 through torch's
+    # float8_e4m3fn, one correctly rounded division in double (the product of
+    # a 2-bit and a 4-bit significand is exact, so there is one rounding).
+    # Row r holds one block: codes 0 .. 15 under scale byte r (0x00 .. 0x7E).
+    s32 = float(np.float32(s_enc))
+    codes = np.tile(np.array([(2 * k) | ((2 * k + 1) << 4) for k in range(8)], np.uint8), (127, 1))
+    scales = np.arange(127, dtype=np.uint8).reshape(127, 1)
+    got = orc.dequantize(codes, scales, s32)
+    e4m3 = torch.from_numpy(scales.ravel().copy()).view(torch.float8_e4m3fn).double().numpy()
+    e2m1 = np.array([e2m1_from_fields(c) for c in range(16)], np.float64)
+    want = (e2m1[None, :] * e4m3[:, None]) / s32
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got[:, 8]), np.ones(127, bool))  # code 8 is -0
