@@ -148,8 +148,9 @@ def cpu_baseline():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
-              "single-GPU by design, see DESIGN.md for how it would shard", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the quantizer and GEMM "
+              "path is measured on one GPU's share of the layer; nothing here uses a second GPU",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
