@@ -356,6 +356,14 @@ def main():
         tf = gemm_flops_one / (ms * 1e-3) / 1e12
         extras["gemm_ex_fprop_bf16_out_amax"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
                                                  "frac_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+
+        # beta-accumulation (gradient accumulation into an fp32 C): C += A B
+        Y32 = torch.zeros(TOKENS, FFN, dtype=torch.float32, device=dev)
+        ms = timed_ms_ev(lambda: nv.gemm_ex(qX, qW, out=Y32, beta=1.0), warm=20)
+        tf = gemm_flops_one / (ms * 1e-3) / 1e12
+        extras["gemm_ex_fprop_f32_beta1"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                                             "frac_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+        del Y32
         qY = nv.Quantized(torch.empty(TOKENS, FFN // 2, dtype=torch.uint8, device=dev),
                           torch.empty(TOKENS, FFN // 16, dtype=torch.uint8, device=dev), tsY)
         ms = timed_ms_ev(lambda: nv.nvfp4_quantize_with_amax(Y16, 0, 0, 0, 0, qY.codes, qY.scales, tsY))
