@@ -116,3 +116,43 @@ def test_gemm_amax_feeds_single_read_quantizer():
     torch.cuda.synchronize()
     for u, v in ((q1.codes, q2.codes), (q1.scales, q2.scales), (q1.tensor_scale, q2.tensor_scale)):
         assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("M,N,K,sampled", [(512, 256, 1024, False), (4096, 4096, 512, True)])
+@pytest.mark.parametrize("beta", [0.0, 0.5])
+def test_gemm_ex_bf16_output_two_byte_aligned(M, N, K, sampled, beta):
+    # a bf16 C that starts 2 bytes into its allocation cannot take the paired
+    # 4-byte stores: the per-value epilogue (half tiles, and whole waves)
+    ah = datagen.host_input(datagen.act(tokens=M, hidden=K, seed=31))
+    bh = datagen.host_input(datagen.weight(out_features=N, in_features=K, seed=32))
+    qa, qb = oracle.quantize_1d(ah), oracle.quantize_1d(bh, rounding=1, seed=6)
+    up = lambda q: nv.Quantized(torch.from_numpy(q[0]).to(DEV), torch.from_numpy(q[1]).to(DEV),
+                                torch.from_numpy(q[2]).to(DEV))
+    if sampled:
+        rng = np.random.default_rng(8)
+        ii = np.concatenate([[0, M - 1], rng.integers(0, M, 3000)]).astype(np.int64)
+        jj = np.concatenate([[0, N - 1], rng.integers(0, N, 3000)]).astype(np.int64)
+        ref, absum = oracle.gemm_sample(qa[0], qa[1], qa[2][0], qb[0], qb[1], qb[2][0], ii, jj)
+    else:
+        ref, absum = oracle.gemm(qa[0], qa[1], qa[2][0], qb[0], qb[1], qb[2][0])
+    g = torch.Generator().manual_seed(9)
+    c_in = (torch.randn(M, N, generator=g) * float(np.abs(ref).max())).to(torch.bfloat16)
+    store = torch.empty(M * N + 1, dtype=torch.bfloat16, device=DEV)
+    c = store[1:].view(M, N)
+    assert c.data_ptr() % 4 == 2
+    c.copy_(c_in.to(DEV))
+    amax = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    nv.gemm_ex(up(qa), up(qb), out=c, beta=beta, amax=amax)
+    torch.cuda.synchronize()
+    got_all = c.float().cpu().numpy()
+    cin = c_in.float().numpy().astype(np.float64)
+    if sampled:
+        got, cin = got_all[ii, jj].astype(np.float64), cin[ii, jj]
+    else:
+        got = got_all.astype(np.float64)
+    want = ref + beta * cin
+    bound = (1e-5 * absum + 2.0 ** -22 * (np.abs(ref) + np.abs(beta * cin))) * (1 + 2.0 ** -8) \
+        + 2.0 ** -8 * np.abs(want)
+    excess = np.abs(got - want) - bound
+    assert excess.max() <= 0, f"max excess {excess.max()}"
+    assert amax.item() == float(np.abs(got_all).max())
