@@ -662,12 +662,14 @@ __global__ __launch_bounds__(kThreads) void k_amax_ct(const void* __restrict__ x
 // column-major and dealt to the eight XCDs in contiguous runs, so the two
 // tiles that complete one 128-byte line of x^T's codes (rows rt and
 // rt + 128) are neighbours in the same L2.
-// At most 128 VGPRs (four waves per SIMD: two workgroups per CU, whose load,
-// encode and write-out phases then overlap); unbounded, the compiler takes
-// about 170 and one workgroup per CU runs the phases back to back (measured
-// 30% slower).
+// bf16 input: at most 128 VGPRs (four waves per SIMD: two workgroups per CU,
+// whose load, encode and write-out phases then overlap); unbounded, the
+// compiler takes about 170 and one workgroup per CU runs the phases back to
+// back (measured 30% slower).  fp32 input holds twice the register data and
+// spilled 57-94 VGPRs under that bound; with two waves per SIMD it takes
+// 149-195 without spills and runs 10-22% faster (measured).
 template <bool BF16, bool SR, bool RHT>
-__global__ __launch_bounds__(kCtThreads, 4) void k_encode_ct(
+__global__ __launch_bounds__(kCtThreads, BF16 ? 4 : 2) void k_encode_ct(
     const void* __restrict__ x, int64_t R, int64_t C, uint64_t seed, uint64_t seed_t, uint32_t stream_t,
     uint32_t rht_mask,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* ts, uint8_t* __restrict__ codes_t,
