@@ -503,15 +503,21 @@ __device__ __forceinline__ void m32_pair(const uint8_t* cur, M32Frag<NT>& f, M32
 }
 
 // One stage from cur.  In: f = step (0, 0), q = raw 0, d = scales.  Out: the
-// same for the stage in nxt; after the barrier, when issue is set, the stage
-// at (m0, n0, k_issue) streams into cur (every wave is done reading it).
+// same for the stage in nxt.  When issue is set, the stage at (m0, n0,
+// k_issue) streams into nxt after the first pair of steps: every wave passed
+// the barrier that ended the previous stage, the last reader of nxt.  The
+// barrier before the last step waits for those loads.  No load is then in
+// flight at a loop back edge, where the compiler's wait insertion would
+// otherwise make the first LDS reads of cur wait for the loads into nxt.
 template <int NT>
 __device__ __forceinline__ void m32_stage(const GemmArgs& g, int64_t m0, int64_t n0, bool issue,
-                                          int64_t k_issue, uint8_t* cur, const uint8_t* nxt, M32Frag<NT>& f,
+                                          int64_t k_issue, const uint8_t* cur, uint8_t* nxt, M32Frag<NT>& f,
                                           M32Raw<NT>& q, M32Scales<NT>& d, floatx16 (&acc)[4][NT], int wm,
                                           int wn, int r, int gq) {
   M32Raw<NT> qn;
   m32_pair<0, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
+  if (issue) m32_issue<NT>(g, m0, n0, k_issue, nxt);
+  __builtin_amdgcn_sched_barrier(0);
   m32_pair<1, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
   m32_pair<2, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
   m32_pair<3, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
@@ -524,7 +530,6 @@ __device__ __forceinline__ void m32_stage(const GemmArgs& g, int64_t m0, int64_t
   m32_order<0, false, NT>();
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // waits for this wave's loads of nxt (vmcnt(0)), then all waves
-  if (issue) m32_issue<NT>(g, m0, n0, k_issue, cur);
   __builtin_amdgcn_sched_barrier(0);
   m32_mfma<NT>(f1, acc);
   m32_read_scales<NT>(nxt, wm, wn, r, gq, d);
@@ -585,7 +590,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_
   const int64_t nk = g.K / kDirBK;  // even
   m32_issue<NT>(g, m0, n0, 0, buf0);
   __syncthreads();
-  m32_issue<NT>(g, m0, n0, kDirBK, buf1);
   M32Frag<NT> f;
   M32Raw<NT> q;
   M32Scales<NT> d;
@@ -593,9 +597,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_
   m32_read_raw<0, NT>(buf0, wm, wn, r, gq, q);
   m32_unpack<0, 0, NT>(q, d, f);
   for (int64_t kt = 0; kt < nk; kt += 2) {
-    m32_stage<NT>(g, m0, n0, kt + 2 < nk, (kt + 2) * kDirBK, buf0, buf1, f, q, d, acc, wm, wn, r, gq);
+    m32_stage<NT>(g, m0, n0, true, (kt + 1) * kDirBK, buf0, buf1, f, q, d, acc, wm, wn, r, gq);
     // on the last stage the reads of buf0 at its end are of stale data and unused
-    m32_stage<NT>(g, m0, n0, kt + 3 < nk, (kt + 3) * kDirBK, buf1, buf0, f, q, d, acc, wm, wn, r, gq);
+    m32_stage<NT>(g, m0, n0, kt + 2 < nk, (kt + 2) * kDirBK, buf1, buf0, f, q, d, acc, wm, wn, r, gq);
   }
 
   // D layout of the 32 x 32 MFMA: lane l, value k -> column l % 32, row
