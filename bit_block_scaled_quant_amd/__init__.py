@@ -111,10 +111,66 @@ def _dtype(x: torch.Tensor):
     raise TypeError("nvfp4: input must be float32 or bfloat16")
 
 
+_U8, _F32 = (torch.uint8,), (torch.float32,)
+_IN = (torch.float32, torch.bfloat16)
+
+
+def _want(t, name, dtypes, device, shape=None, min_numel=None, optional=False):
+    """Check one tensor argument before any pointer reaches the library: its
+    dtype, its exact shape (or at least min_numel elements), its device and
+    its layout.  An undersized or mistyped output would otherwise be written
+    past its end by a kernel."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"nvfp4: {name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"nvfp4: {name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"nvfp4: {name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"nvfp4: {name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"nvfp4: {name} needs at least {min_numel} elements, got {t.numel()}")
+    if t.device != device:
+        raise ValueError(f"nvfp4: {name} is on {t.device}, the call's tensors are on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"nvfp4: {name} must be contiguous")
+
+
+def _want_input(x, name="x"):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"nvfp4: {name} must be a 2-D tensor")
+    _want(x, name, _IN, x.device)
+    return x.shape[0], x.shape[1], x.device
+
+
+def _want_quantized(rows, cols, device, codes, scales, tensor_scale, codes_t=None, scales_t=None,
+                    block=16, transposed_optional=True):
+    _want(codes, "codes", _U8, device, (rows, cols // 2))
+    _want(scales, "scales", _U8, device, (rows, cols // block))
+    if tensor_scale is not None or block == 16:
+        _want(tensor_scale, "tensor_scale", _F32, device, min_numel=2)
+    if (codes_t is None) != (scales_t is None):
+        raise ValueError("nvfp4: codes_t and scales_t go together (both or neither)")
+    if codes_t is None and not transposed_optional:
+        raise ValueError("nvfp4: codes_t and scales_t are required")
+    _want(codes_t, "codes_t", _U8, device, (cols, rows // 2), optional=True)
+    _want(scales_t, "scales_t", _U8, device, (cols, rows // 16), optional=True)
+
+
+def _want_gemm_operands(a_codes, a_scales, b_codes, b_scales, M, N, K, device, block=16):
+    _want(a_codes, "a_codes", _U8, device, (M, K // 2))
+    _want(a_scales, "a_scales", _U8, device, (M, K // block))
+    _want(b_codes, "b_codes", _U8, device, (N, K // 2))
+    _want(b_scales, "b_scales", _U8, device, (N, K // block))
+
+
 # ---- entry points with the C names (argument marshalling only) ----------
 def nvfp4_quantize(x, rounding, seed, rht, rht_seed, codes, scales, tensor_scale,
                    codes_t=None, scales_t=None):
-    rows, cols = x.shape
+    rows, cols, dev = _want_input(x)
+    _want_quantized(rows, cols, dev, codes, scales, tensor_scale, codes_t, scales_t)
     _check(lib().nvfp4_quantize(_ptr(x), _dtype(x), rows, cols, int(rounding), int(seed),
                                 int(rht), int(rht_seed), _ptr(codes), _ptr(scales),
                                 _ptr(tensor_scale), _ptr(codes_t), _ptr(scales_t), _stream(x)),
@@ -122,7 +178,8 @@ def nvfp4_quantize(x, rounding, seed, rht, rht_seed, codes, scales, tensor_scale
 
 
 def nvfp4_quantize_2d(w, rounding, seed, codes, scales, tensor_scale, codes_t=None, scales_t=None):
-    rows, cols = w.shape
+    rows, cols, dev = _want_input(w, "w")
+    _want_quantized(rows, cols, dev, codes, scales, tensor_scale, codes_t, scales_t)
     _check(lib().nvfp4_quantize_2d(_ptr(w), _dtype(w), rows, cols, int(rounding), int(seed),
                                    _ptr(codes), _ptr(scales), _ptr(tensor_scale), _ptr(codes_t),
                                    _ptr(scales_t), _stream(w)), "nvfp4_quantize_2d")
@@ -130,7 +187,10 @@ def nvfp4_quantize_2d(w, rounding, seed, codes, scales, tensor_scale, codes_t=No
 
 def nvfp4_quantize_cast_transpose(x, rounding, seed, seed_t, rht_t, rht_seed, codes, scales, tensor_scale,
                                   codes_t, scales_t, tensor_scale_t):
-    rows, cols = x.shape
+    rows, cols, dev = _want_input(x)
+    _want_quantized(rows, cols, dev, codes, scales, tensor_scale, codes_t, scales_t,
+                    transposed_optional=False)
+    _want(tensor_scale_t, "tensor_scale_t", _F32, dev, min_numel=2)
     _check(lib().nvfp4_quantize_cast_transpose(
         _ptr(x), _dtype(x), rows, cols, int(rounding), int(seed), int(seed_t), int(rht_t), int(rht_seed),
         _ptr(codes), _ptr(scales), _ptr(tensor_scale), _ptr(codes_t), _ptr(scales_t), _ptr(tensor_scale_t),
@@ -138,17 +198,24 @@ def nvfp4_quantize_cast_transpose(x, rounding, seed, seed_t, rht_t, rht_seed, co
 
 
 def nvfp4_rht(x, rht_seed, y):
-    rows, cols = x.shape
+    rows, cols, dev = _want_input(x)
+    _want(y, "y", _F32, dev, (rows, cols))
     _check(lib().nvfp4_rht(_ptr(x), _dtype(x), rows, cols, int(rht_seed), _ptr(y), _stream(x)),
            "nvfp4_rht")
 
 
 def nvfp4_dequantize(codes, scales, tensor_scale, rows, cols, out):
+    _want(out, "out", _IN, out.device if isinstance(out, torch.Tensor) else None, (rows, cols))
+    _want_quantized(rows, cols, out.device, codes, scales, tensor_scale)
     _check(lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(tensor_scale), int(rows), int(cols),
                                   _dtype(out), _ptr(out), _stream(out)), "nvfp4_dequantize")
 
 
 def nvfp4_gemm(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, M, N, K, c):
+    _want(c, "c", _F32, c.device if isinstance(c, torch.Tensor) else None, (M, N))
+    _want_gemm_operands(a_codes, a_scales, b_codes, b_scales, M, N, K, c.device)
+    _want(a_tensor_scale, "a_tensor_scale", _F32, c.device, min_numel=1)
+    _want(b_tensor_scale, "b_tensor_scale", _F32, c.device, min_numel=1)
     _check(lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_codes),
                             _ptr(b_scales), _ptr(b_tensor_scale), int(M), int(N), int(K), _ptr(c),
                             _stream(c)), "nvfp4_gemm")
@@ -156,30 +223,41 @@ def nvfp4_gemm(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_sc
 
 def nvfp4_gemm_ex(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, M, N, K, c,
                   beta=0.0, c_amax=None):
+    _want(c, "c", _IN, c.device if isinstance(c, torch.Tensor) else None, (M, N))
+    _want_gemm_operands(a_codes, a_scales, b_codes, b_scales, M, N, K, c.device)
+    _want(a_tensor_scale, "a_tensor_scale", _F32, c.device, min_numel=1)
+    _want(b_tensor_scale, "b_tensor_scale", _F32, c.device, min_numel=1)
+    _want(c_amax, "c_amax", _F32, c.device, min_numel=1, optional=True)
     _check(lib().nvfp4_gemm_ex(_ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_codes),
                                _ptr(b_scales), _ptr(b_tensor_scale), int(M), int(N), int(K), _ptr(c),
                                _dtype(c), float(beta), _ptr(c_amax), _stream(c)), "nvfp4_gemm_ex")
 
 
 def nvfp4_quantize_with_amax(x, rounding, seed, rht, rht_seed, codes, scales, tensor_scale):
-    rows, cols = x.shape
+    rows, cols, dev = _want_input(x)
+    _want_quantized(rows, cols, dev, codes, scales, tensor_scale)
     _check(lib().nvfp4_quantize_with_amax(_ptr(x), _dtype(x), rows, cols, int(rounding), int(seed), int(rht),
                                           int(rht_seed), _ptr(codes), _ptr(scales), _ptr(tensor_scale),
                                           _stream(x)), "nvfp4_quantize_with_amax")
 
 
 def mxfp4_quantize(x, codes, scales):
-    rows, cols = x.shape
+    rows, cols, dev = _want_input(x)
+    _want_quantized(rows, cols, dev, codes, scales, None, block=32)
     _check(lib().mxfp4_quantize(_ptr(x), _dtype(x), rows, cols, _ptr(codes), _ptr(scales), _stream(x)),
            "mxfp4_quantize")
 
 
 def mxfp4_dequantize(codes, scales, rows, cols, out):
+    _want(out, "out", _IN, out.device if isinstance(out, torch.Tensor) else None, (rows, cols))
+    _want_quantized(rows, cols, out.device, codes, scales, None, block=32)
     _check(lib().mxfp4_dequantize(_ptr(codes), _ptr(scales), int(rows), int(cols), _dtype(out), _ptr(out),
                                   _stream(out)), "mxfp4_dequantize")
 
 
 def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, c):
+    _want(c, "c", _F32, c.device if isinstance(c, torch.Tensor) else None, (M, N))
+    _want_gemm_operands(a_codes, a_scales, b_codes, b_scales, M, N, K, c.device, block=32)
     _check(lib().mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), int(M), int(N),
                             int(K), _ptr(c), _stream(c)), "mxfp4_gemm")
 
