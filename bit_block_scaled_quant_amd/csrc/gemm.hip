@@ -58,11 +58,21 @@ __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ 
 // (b & 0x7F) << 7, which is its value times 2^-8 (subnormal E4M3 bytes become
 // fp16 subnormals), so one packed multiply yields code * scale exactly: the
 // product has at most 6 significant bits and lies in [2^-10, 2688].
+//
+// The four conversions go to four registers before any multiply: written as
+// one conversion-multiply pair per byte, the compiler reused one temporary
+// register, so every multiply waited on the conversion just before it and
+// the next conversion on that multiply.
 __device__ __forceinline__ half8 unpack8(uint32_t w, half2v sc) {
-  const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * sc;
-  const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * sc;
-  const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * sc;
-  const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * sc;
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0);
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1);
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2);
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3);
+  asm volatile("" : "+v"(p0), "+v"(p1), "+v"(p2), "+v"(p3));  // all four are live at once
+  p0 = p0 * sc;
+  p1 = p1 * sc;
+  p2 = p2 * sc;
+  p3 = p3 * sc;
   return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
