@@ -270,6 +270,30 @@ def gemm_sample(a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, ii, jj):
     return c, cabs
 
 
+def gemm_dense(a_codes, a_scales, a_s_enc, b_codes, b_scales, b_s_enc, rows=None, chunk=1024):
+    """The GEMM definition for every output of a large product: each operand
+    is dequantized by the oracle's per-element rule (``dequantize``, the
+    value e2m1 * e4m3 / S of every element, in double), and the two are
+    contracted in float64 by numpy's matrix product, which also gives
+    sum_k |a_ik b_jk| as |A| |B|^T.  Only the order of the double-precision
+    additions differs from ``gemm`` (relative difference ~1e-13, far inside
+    any fp32 tolerance).  rows (optional) selects the output rows; A is
+    processed ``chunk`` rows at a time.  Returns (C, sum |ab|)."""
+    a = dequantize(a_codes, a_scales, a_s_enc)
+    b = dequantize(b_codes, b_scales, b_s_enc)
+    if rows is not None:
+        a = a[np.asarray(rows)]
+    bt, bat = np.ascontiguousarray(b.T), np.ascontiguousarray(np.abs(b).T)
+    del b
+    c = np.empty((a.shape[0], bt.shape[1]), dtype=np.float64)
+    cabs = np.empty_like(c)
+    for r0 in range(0, a.shape[0], chunk):
+        blk = a[r0:r0 + chunk]
+        np.matmul(blk, bt, out=c[r0:r0 + chunk])
+        np.matmul(np.abs(blk), bat, out=cabs[r0:r0 + chunk])
+    return c, cabs
+
+
 def num_threads():
     return lib().orc_num_threads()
 

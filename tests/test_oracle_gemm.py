@@ -111,3 +111,23 @@ def test_tiny_pipeline_information_only(orc):
     # NVFP4 keeps a few percent of relative error on outlier-heavy data; this
     # is a sanity bound (not a parity claim): a broken scale path gives ~1.
     assert rel < 0.2
+
+
+@pytest.mark.parametrize("M,N,K,chunk", [(37, 29, 160, 8), (64, 48, 512, 1024)])
+def test_gemm_dense_equals_definition(orc, M, N, K, chunk):
+    # the dense form (oracle dequantization contracted by a float64 matmul)
+    # against the definition (double sum per output): only the order of the
+    # double additions differs
+    rng = np.random.default_rng(M)
+    ac, asc = random_operand(rng, M, K)
+    bc, bsc = random_operand(rng, N, K)
+    sa, sb = np.float32(0.37), np.float32(1234.5)
+    c, cabs = orc.gemm(ac, asc, sa, bc, bsc, sb)
+    d, dabs = orc.gemm_dense(ac, asc, sa, bc, bsc, sb, chunk=chunk)
+    assert np.all(np.abs(c - d) <= 1e-13 * cabs)
+    assert np.allclose(cabs, dabs, rtol=1e-13, atol=0)
+    rows = np.array([0, M - 1, M // 2])
+    e, eabs = orc.gemm_dense(ac, asc, sa, bc, bsc, sb, rows=rows)
+    # (BLAS may block a row subset differently: the same bound, not bit equality)
+    assert np.all(np.abs(e - c[rows]) <= 1e-13 * cabs[rows])
+    assert np.allclose(eabs, cabs[rows], rtol=1e-13, atol=0)
