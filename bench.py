@@ -50,8 +50,9 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--extras", choices=("all", "none", "only", "sweep"), default="all",
                    help="measurements outside the step (quantizer sweep, dequantize, MXFP4, "
-                        "epilogue options): all (default), none, only those (one untimed step "
-                        "first; prints just the extras), or only the quantizer sweep")
+                        "epilogue options, the Tiny workload): all (default), none, only those "
+                        "(one untimed step first; prints just the extras), or only the quantizer "
+                        "sweep")
     p.add_argument("--graph", action="store_true",
                    help="time the step as replays of one HIP graph instead of eager launches "
                         "(measured +0.2%%: the launches already overlap)")
@@ -143,9 +144,50 @@ def cpu_baseline():
         t_total += per_mac * M * N * K
         detail.append(f"{name}: {s} outputs x {HIDDEN} MACs")
     flops = 3 * 2.0 * TOKENS * FFN * HIDDEN
+    # cores: the OpenMP threads the oracle ran with; host_cpus: the logical
+    # CPUs of the host and those this process may run on
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "host_cpus": os.cpu_count(),
+            "host_cpus_available": len(os.sched_getaffinity(0)),
             "sample": "; ".join(detail) + f"; extrapolated step time {t_total:.1f} s"}
+
+
+def tiny_times(nv, datagen, torch, dev, reps=50):
+    """The Tiny workload (A, B [256 x 256] fp32, 1% x50 outliers, seed 0, both
+    quantized 1D with RNE, then C = A . B^T): median launch-to-completion
+    time of each call over reps runs, by HIP events on the launch stream.
+    Latency-bound (one or two waves of work), so no roofline claim."""
+    a = datagen.tiny(dev, seed=0, tag=datagen.TAG_A)
+    b = datagen.tiny(dev, seed=0, tag=datagen.TAG_B)
+    qa, qb = nv.quantize(a), nv.quantize(b)
+    c = torch.empty(256, 256, dtype=torch.float32, device=dev)
+    calls = {"quantize_A": lambda: nv.nvfp4_quantize(a, 0, 0, 0, 0, qa.codes, qa.scales, qa.tensor_scale),
+             "quantize_B": lambda: nv.nvfp4_quantize(b, 0, 0, 0, 0, qb.codes, qb.scales, qb.tensor_scale),
+             "gemm": lambda: nv.gemm(qa, qb, out=c)}
+    out = {}
+    for name, fn in calls.items():
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        out[name + "_us"] = round(float(np.median(ts)), 2)
+    # the whole pass, back to back
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for fn in calls.values():
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    out["pass_us"] = round(float(np.median(ts)), 2)
+    out["shape"] = "A, B [256 x 256] fp32; C = A . B^T 256 x 256 x 256"
+    return out
 
 
 def main():
@@ -178,6 +220,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     seed = args.seed
+    # dY^T's stochastic rounding draws from a key of its own, so the two SR
+    # copies of dY (dgrad's and wgrad's) use independent random bits
+    seed_t = seed + 1
     X = datagen.act(dev, seed=seed)
     W = datagen.weight(dev, seed=seed)
     dY = datagen.grad(dev, seed=seed)
@@ -222,7 +267,7 @@ def main():
              qmeta(TOKENS, FFN, 2, False)),
             gemm_dgrad,
             ("quant_dYt_1d_sr_rht", "quant", lambda: nv.nvfp4_quantize(
-                dYt, 1, seed, 1, seed, qdYt.codes, qdYt.scales, qdYt.tensor_scale),
+                dYt, 1, seed_t, 1, seed, qdYt.codes, qdYt.scales, qdYt.tensor_scale),
              qmeta(FFN, TOKENS, 2, False)),
             ("quant_Xt_1d_rne_rht", "quant", lambda: nv.nvfp4_quantize(
                 Xt, 0, 0, 1, seed, qXt.codes, qXt.scales, qXt.tensor_scale),
@@ -237,7 +282,7 @@ def main():
                 qXt.tensor_scale), qmeta(TOKENS, HIDDEN, 2, True)),
             quant_W, gemm_fprop,
             ("ct_dY_sr_rht", "quant", lambda: nv.nvfp4_quantize_cast_transpose(
-                dY, 1, seed, seed, 1, seed, qdY.codes, qdY.scales, qdY.tensor_scale, qdYt.codes,
+                dY, 1, seed, seed_t, 1, seed, qdY.codes, qdY.scales, qdY.tensor_scale, qdYt.codes,
                 qdYt.scales, qdYt.tensor_scale), qmeta(TOKENS, FFN, 2, True)),
             gemm_dgrad, gemm_wgrad,
         ]
@@ -254,9 +299,13 @@ def main():
         """The quantizer-only bandwidth sweep: bf16 N(0,1) with 0.1% of the
         entries x100 at three shapes, each quantized 1D with its columnwise
         copy and 2D with its transposed copy, with RNE and with SR.  Every
-        timed call starts from a cold cache: a 512 MiB write evicts the input
-        from L2 and the 256 MB MALL first.  The time is the median of the
-        calls (HIP events on the launch stream around the call alone)."""
+        timed call starts from a cold cache: a 512 MiB write and then a read
+        of those 512 MiB evict the input from L2 and the 256 MB MALL first.
+        The read leaves the caches holding clean lines only: after the write
+        alone, the timed call would also pay for writing the flush's dirty
+        lines back to HBM (measured: 10-30 us on the large calls).  The time
+        is the median of the calls (HIP events on the launch stream around
+        the call alone)."""
         flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev)
         res = {}
         for rows, cols in ((TOKENS, HIDDEN), (TOKENS, FFN), (4 * TOKENS, HIDDEN)):
@@ -274,12 +323,14 @@ def main():
                     ts = []
                     for _ in range(reps):
                         flush.fill_(float(len(ts)))
+                        flush_sum = flush.sum()  # reads the 512 MiB back: evicts the dirty lines
                         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                         a.record()
                         fn()
                         b.record()
                         torch.cuda.synchronize()
                         ts.append(a.elapsed_time(b))
+                    del flush_sum
                     ms = float(np.median(ts))
                     qm = qmeta(rows, cols, 2, True)
                     gbs = qm["alg"] / (ms * 1e-3) / 1e9
@@ -313,7 +364,8 @@ def main():
 
     def run_extras():
         """Measurements outside the step (not part of value)."""
-        extras = {"copy_1GiB": copy_bandwidth(), "quantizer_sweep": run_sweep()}
+        extras = {"copy_1GiB": copy_bandwidth(), "quantizer_sweep": run_sweep(),
+                  "tiny": tiny_times(nv, datagen, torch, dev)}
         # outside the step: dequantization of dY's rowwise copy (HBM-bound)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         gemm_flops_one = 2.0 * TOKENS * FFN * HIDDEN
@@ -409,23 +461,6 @@ def main():
                                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         del Wt, dYt_m, Xt_m, mxq, qa
 
-        # context, not part of the path: the vendor library's plain fp16 and
-        # bf16 GEMM (torch.matmul -> hipBLASLt) on the same three shapes, with
-        # already-dequantized 16-bit operands and a 16-bit output (no unpack,
-        # half the output bytes of the fp32 C above)
-        lib = {}
-        for name, (M, N, K) in (("fprop", (TOKENS, FFN, HIDDEN)), ("dgrad", (TOKENS, HIDDEN, FFN)),
-                                ("wgrad", (FFN, HIDDEN, TOKENS))):
-            for dt, tag in ((torch.float16, "fp16"), (torch.bfloat16, "bf16")):
-                a16 = torch.randn(M, K, device=dev, dtype=dt)
-                b16 = torch.randn(N, K, device=dev, dtype=dt)
-                c16 = torch.empty(M, N, device=dev, dtype=dt)
-                ms = timed_ms(lambda: torch.matmul(a16, b16.t(), out=c16), warm=20)
-                lib[f"{name}_{tag}"] = {"ms": round(ms, 4),
-                                        "TFLOP/s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
-                del a16, b16, c16
-        extras["library_gemm_16bit_reference"] = lib
-
         def rel_err(t, deq):
             d = (deq.double() - t.double())
             return float(torch.linalg.vector_norm(d) / torch.linalg.vector_norm(t.double()))
@@ -484,13 +519,19 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # per-call durations with HIP events on the launch stream
+    # per-call durations with HIP events on the launch stream, recorded over
+    # K steps launched back to back and read after one synchronization: each
+    # call's start event then completes when the previous call does, so host
+    # launch latency (an idle GPU waiting for the next launch) is not counted
     per_call = {name: [] for name, _, _, _ in calls}
+    step_events = []
     for _ in range(args.steps):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in calls]
         step(ev)
-        torch.cuda.synchronize()
+        step_events.append(ev)
+    torch.cuda.synchronize()
+    for ev in step_events:
         for (name, _, _, _), (a, b) in zip(calls, ev):
             per_call[name].append(a.elapsed_time(b))
 
@@ -502,7 +543,7 @@ def main():
     gemm_ms = []
     quant_ms_total, quant_bytes_total = 0.0, 0.0
     for name, kind, _, meta in calls:
-        ms = float(np.mean(per_call[name]))
+        ms = float(np.median(per_call[name]))
         if kind == "gemm":
             M, N, K = meta
             tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12

@@ -35,18 +35,15 @@ namespace nvfp4 {
 constexpr float kFltMax = 3.40282346638528859812e+38f;
 
 // ---------------------------------------------------------------- E4M3 ---
-// s >= 0, finite or +inf.  Round to nearest even, saturate to 448 (0x7E).
-// Both ranges are computed and selected, so a wavefront does not diverge.
+// s >= 0, finite or +inf.  Round to nearest even, saturate to 448 (0x7E):
+// gfx950's fp8 conversion (OCP E4M3, round to nearest even, subnormals kept)
+// of min(s, 448).  A device probe found it equal to a bit-level
+// round-to-nearest-even encoder for every non-negative fp32 pattern up to
+// +inf; the tests check the scale bytes of the quantizers against the
+// oracle's argmin encoder, around every E4M3 rounding boundary and over
+// whole tensors.
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  const uint32_t b = __float_as_uint(s);
-  // s < 2^-6: subnormal range, multiples of 2^-9; s * 512 is exact and
-  // rintf rounds half to even (8 is the smallest normal)
-  const uint32_t sub = (uint32_t)__builtin_rintf(s * 512.0f);
-  // otherwise keep 3 mantissa bits, round to nearest even on the discarded 20
-  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
-  const uint32_t nrm = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);  // exponent bias 7
-  const uint32_t v = b < 0x3C800000u ? sub : nrm;
-  return s < 448.0f ? v : 0x7Eu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t byte) {
@@ -68,8 +65,8 @@ __device__ __forceinline__ float tensor_scale_from_amax(float amax) {
 // is the correctly rounded quotient for every t in [2^-125, FLT_MAX] (checked
 // exhaustively on the host over all those bit patterns).  Below 2^-125 it may
 // miss by an ulp of a subnormal, and +inf gives NaN: in both cases the E4M3
-// byte of the quotient is unchanged (0x00 below 2^-10; 0x7E, since the
-// saturation test is false for inf and NaN alike).
+// byte of the quotient is unchanged (0x00 below 2^-10; 0x7E, since
+// min(NaN, 448) is 448).
 __device__ __forceinline__ float div6(float t) {
   const float c = 0.16666667163372039795f;  // fl(1/6)
   const float q0 = t * c;

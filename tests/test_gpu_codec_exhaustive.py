@@ -149,3 +149,35 @@ def test_device_encoder_saturation_range(rounding):
     assert np.array_equal(want & 7, np.full(body.size, 7))  # saturated: magnitude 6
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, f"{bad.size} mismatches, e.g. y={body[bad[:4]]} got={got[bad[:4]]}"
+
+
+@pytest.mark.timeout(600)
+def test_block_scale_bytes_at_every_e4m3_boundary():
+    """The block scale byte (E4M3 of amax_b * S_enc / 6, round to nearest
+    even, saturating at 448) around every rounding boundary of E4M3: rows
+    [a, 0, ..., 0] with a tensor maximum of 2688 elsewhere (S_enc = 1), so the
+    byte is E4M3(fl(a / 6)).  For every midpoint m between neighbouring E4M3
+    values (and the saturation point 464), a runs over the 257 fp32 values
+    around fl(6 m); plus a million random block maxima in (0, 2688].  Scale
+    bytes and codes must equal the oracle's."""
+    vals = np.array(sorted({oracle.e4m3_value(b) for b in range(0x7F)}))
+    mids = np.concatenate([(vals[:-1] + vals[1:]) / 2, [464.0]])
+    centers = (6.0 * mids).astype(np.float32).view(np.int32)
+    near = (centers[:, None] + np.arange(-128, 129)[None, :]).reshape(-1)
+    near = near[(near > 0) & (near <= np.float32(2688.0).view(np.int32))].view(np.float32)
+    rng = np.random.default_rng(5)
+    rand = rng.uniform(0.0, 2688.0, 1 << 20).astype(np.float32)
+    rand = np.concatenate([rand, np.exp2(rng.uniform(-40, 11.39, 1 << 18)).astype(np.float32)])
+    a = np.concatenate([near, rand])
+    a = a[(a > 0) & (a <= 2688.0)]
+    x = np.zeros((a.size + 1, 16), dtype=np.float32)
+    x[:-1, 0] = a
+    x[-1, 0] = 2688.0
+    q = nv.quantize(torch.from_numpy(x).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.quantize_1d(x)
+    assert ref[2][0] == 1.0
+    for got, want, name in ((q.scales, ref[1], "scales"), (q.codes, ref[0], "codes")):
+        g = got.cpu().numpy()
+        bad = np.argwhere(g != want)
+        assert bad.size == 0, f"{name}: {len(bad)} mismatches, e.g. a={a[bad[:4, 0]]} got={g[tuple(bad[:4].T)]}"
