@@ -359,50 +359,65 @@ struct M32Scales { uint4 a[2], b[(NT + 1) / 2]; };  // dword 2i + q: blocks 8g +
 // Scale slots of an operand with 2 x NT tile-rows per wave half (A: NT = 4):
 // slot ((2g + w) * 32 + r) * 2NT + 2i + q holds the four scale bytes of blocks
 // 8g + 4q .. 8g + 4q + 3 of row (rows / 2) w + 32 i + r.
-template <int NT>
-__device__ __forceinline__ void m32_issue_scales(const uint8_t* s0, int64_t ks, uint8_t* dst) {
+template <int NT, int V>
+__device__ __forceinline__ void m32_issue_scale_slot(const uint8_t* s0, int64_t ks, uint8_t* dst) {
   constexpr int kLog = NT == 4 ? 2 : 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int v = 0; v < NT; ++v) {
-    const int slot = 256 * v + 64 * wave + lane;
-    const int q = slot & 1, i = (slot >> 1) & (NT - 1), r = (slot >> (1 + kLog)) & 31;
-    const int w = (slot >> (6 + kLog)) & 1, gg = slot >> (7 + kLog);
-    const int row = 32 * NT * w + 32 * i + r;
-    const uint32_t off = (uint32_t)(row * ks + 4 * (2 * gg + q));
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(s0 + off), (lds_void_t*)(dst + 1024 * v + 256 * wave), 4,
+  const int slot = 256 * V + 64 * wave + lane;
+  const int q = slot & 1, i = (slot >> 1) & (NT - 1), r = (slot >> (1 + kLog)) & 31;
+  const int w = (slot >> (6 + kLog)) & 1, gg = slot >> (7 + kLog);
+  const int row = 32 * NT * w + 32 * i + r;
+  const uint32_t off = (uint32_t)(row * ks + 4 * (2 * gg + q));
+  __builtin_amdgcn_global_load_lds((glb_void_t*)(s0 + off), (lds_void_t*)(dst + 1024 * V + 256 * wave), 4, 0, 0);
+}
+
+// Part U (0..7) of a stage's loads: A block 8 * wave + U, B block
+// 2 NT * wave + U (U < 2 NT), and one scale slot group (A: U < 4; B:
+// 4 <= U < 4 + NT).  A stage is issued as eight such parts spread over the
+// first four step pairs: issued all at once, the 24 loads of every wave
+// backed up in the texture unit and stalled the waves' MFMA issue (about 57
+// cycles per load instruction, by counters).
+template <int NT, int U>
+__device__ __forceinline__ void m32_issue_part(const GemmArgs& g, int64_t m0, int64_t n0, int64_t k0,
+                                               uint8_t* buf) {
+  using L = M32<NT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t kb = g.K / 2, ks = g.K / 16;
+  {
+    const uint8_t* a0 = g.a_codes + m0 * kb + k0 / 2;
+    const int blk = 8 * wave + U;
+    const int row = 8 * blk + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    const uint32_t off = (uint32_t)(row * kb + 16 * chunk);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(a0 + off), (lds_void_t*)(buf + 1024 * blk), 16, 0, 0);
+  }
+  if (U < 2 * NT) {
+    const uint8_t* b0 = g.b_codes + n0 * kb + k0 / 2;
+    const int bb = 2 * NT * wave + U, brow = 8 * bb + (lane >> 3);
+    const int bchunk = (lane & 7) ^ ((brow ^ (brow >> 3)) & 7);
+    const uint32_t boff = (uint32_t)(brow * kb + 16 * bchunk);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(b0 + boff), (lds_void_t*)(buf + L::kOffB + 1024 * bb), 16,
                                      0, 0);
   }
+  if (U < 4)
+    m32_issue_scale_slot<4, U>(g.a_scales + m0 * ks + k0 / 16, ks, buf + L::kOffAS);
+  else if (U < 4 + NT)
+    m32_issue_scale_slot<NT, U - 4>(g.b_scales + n0 * ks + k0 / 16, ks, buf + L::kOffBS);
 }
 
 template <int NT>
 __device__ __forceinline__ void m32_issue(const GemmArgs& g, int64_t m0, int64_t n0, int64_t k0,
                                           uint8_t* buf) {
-  using L = M32<NT>;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t kb = g.K / 2, ks = g.K / 16;
-  const uint8_t* a0 = g.a_codes + m0 * kb + k0 / 2;
-  const uint8_t* b0 = g.b_codes + n0 * kb + k0 / 2;
-  // 1 KB blocks of 8 rows: 32 for A, 8 NT for B
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int blk = 8 * wave + u;
-    const int row = 8 * blk + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
-    const uint32_t off = (uint32_t)(row * kb + 16 * chunk);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(a0 + off), (lds_void_t*)(buf + 1024 * blk), 16, 0, 0);
-    if (u < 2 * NT) {
-      const int bb = 2 * NT * wave + u, brow = 8 * bb + (lane >> 3);
-      const int bchunk = (lane & 7) ^ ((brow ^ (brow >> 3)) & 7);
-      const uint32_t boff = (uint32_t)(brow * kb + 16 * bchunk);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(b0 + boff), (lds_void_t*)(buf + L::kOffB + 1024 * bb),
-                                       16, 0, 0);
-    }
-  }
-  m32_issue_scales<4>(g.a_scales + m0 * ks + k0 / 16, ks, buf + L::kOffAS);
-  m32_issue_scales<NT>(g.b_scales + n0 * ks + k0 / 16, ks, buf + L::kOffBS);
+  m32_issue_part<NT, 0>(g, m0, n0, k0, buf);
+  m32_issue_part<NT, 1>(g, m0, n0, k0, buf);
+  m32_issue_part<NT, 2>(g, m0, n0, k0, buf);
+  m32_issue_part<NT, 3>(g, m0, n0, k0, buf);
+  m32_issue_part<NT, 4>(g, m0, n0, k0, buf);
+  m32_issue_part<NT, 5>(g, m0, n0, k0, buf);
+  m32_issue_part<NT, 6>(g, m0, n0, k0, buf);
+  m32_issue_part<NT, 7>(g, m0, n0, k0, buf);
 }
 
 template <int NT>
@@ -526,11 +541,29 @@ __device__ __forceinline__ void m32_stage(const GemmArgs& g, int64_t m0, int64_t
                                           int wn, int r, int gq) {
   M32Raw<NT> qn;
   m32_pair<0, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
-  if (issue) m32_issue<NT>(g, m0, n0, k_issue, nxt);
+  if (issue) {
+    m32_issue_part<NT, 0>(g, m0, n0, k_issue, nxt);
+    m32_issue_part<NT, 1>(g, m0, n0, k_issue, nxt);
+  }
   __builtin_amdgcn_sched_barrier(0);
   m32_pair<1, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
+  if (issue) {
+    m32_issue_part<NT, 2>(g, m0, n0, k_issue, nxt);
+    m32_issue_part<NT, 3>(g, m0, n0, k_issue, nxt);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   m32_pair<2, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
+  if (issue) {
+    m32_issue_part<NT, 4>(g, m0, n0, k_issue, nxt);
+    m32_issue_part<NT, 5>(g, m0, n0, k_issue, nxt);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   m32_pair<3, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
+  if (issue) {
+    m32_issue_part<NT, 6>(g, m0, n0, k_issue, nxt);
+    m32_issue_part<NT, 7>(g, m0, n0, k_issue, nxt);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   m32_pair<4, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
   m32_pair<5, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
   m32_pair<6, NT>(cur, f, q, qn, d, acc, wm, wn, r, gq);
