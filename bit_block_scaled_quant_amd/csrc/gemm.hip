@@ -312,9 +312,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 //  - A stage holds 256 K-elements of both operands (128 code bytes and 16
 //    scale bytes per row, 72 KB); two stages are double buffered in LDS.
 //  - Operand bytes go from global memory straight into LDS
-//    (global_load_lds_dwordx4 for codes, _dword for scales): no staging
-//    registers and no LDS store instructions.  Code rows are 8 XOR-swizzled
-//    16-byte chunks, so the 8 rows a wave reads at once hit distinct banks.
+//    (global_load_lds_dwordx4, 16 bytes per lane): no staging registers and
+//    no LDS store instructions.  Code rows are 8 XOR-swizzled 16-byte
+//    chunks, so the 8 rows a wave reads at once hit distinct banks.
 //  - Four waves, one per SIMD, each own 128 x 128 of the 256 x 256 tile as
 //    4 x 4 tiles of v_mfma_f32_32x32x16_f16 (accumulators in AGPRs).
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -356,25 +356,23 @@ struct M32Raw { uint4 a[4], b[NT]; };  // blocks 8g + 2Q (.x, .y) and 8g + 2Q + 
 template <int NT>
 struct M32Scales { uint4 a[2], b[(NT + 1) / 2]; };  // dword 2i + q: blocks 8g + 4q .. + 3 of tile-row i
 
-// Scale slots of an operand with 2 x NT tile-rows per wave half (A: NT = 4):
-// slot ((2g + w) * 32 + r) * 2NT + 2i + q holds the four scale bytes of blocks
-// 8g + 4q .. 8g + 4q + 3 of row (rows / 2) w + 32 i + r.
-template <int NT, int V>
-__device__ __forceinline__ void m32_issue_scale_slot(const uint8_t* s0, int64_t ks, uint8_t* dst) {
-  constexpr int kLog = NT == 4 ? 2 : 1;
+// A stage's scale bytes sit in LDS in their global order: row r's 16 bytes
+// (blocks 0 .. 15 of the stage) at 16 r.  A wave loads 64 rows with one
+// 16-byte-per-lane load (with 4-byte loads into a lane-shuffled layout a
+// stage took 4 + NT load instructions per wave instead of 1 + 1, and every
+// load instruction costs issue cycles beside the MFMAs).
+template <int ROWS>
+__device__ __forceinline__ void m32_issue_scales(const uint8_t* s0, int64_t ks, uint8_t* dst) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int slot = 256 * V + 64 * wave + lane;
-  const int q = slot & 1, i = (slot >> 1) & (NT - 1), r = (slot >> (1 + kLog)) & 31;
-  const int w = (slot >> (6 + kLog)) & 1, gg = slot >> (7 + kLog);
-  const int row = 32 * NT * w + 32 * i + r;
-  const uint32_t off = (uint32_t)(row * ks + 4 * (2 * gg + q));
-  __builtin_amdgcn_global_load_lds((glb_void_t*)(s0 + off), (lds_void_t*)(dst + 1024 * V + 256 * wave), 4, 0, 0);
+  if (64 * wave >= ROWS) return;  // wave-uniform: a 128-row operand takes two waves
+  const uint32_t off = (uint32_t)((64 * wave + lane) * ks);
+  __builtin_amdgcn_global_load_lds((glb_void_t*)(s0 + off), (lds_void_t*)(dst + 1024 * wave), 16, 0, 0);
 }
 
 // Part U (0..7) of a stage's loads: A block 8 * wave + U, B block
-// 2 NT * wave + U (U < 2 NT), and one scale slot group (A: U < 4; B:
-// 4 <= U < 4 + NT).  A stage is issued as eight such parts spread over the
+// 2 NT * wave + U (U < 2 NT), and with U = 0 / 1 the wave's rows of A / B
+// scales.  A stage is issued as eight such parts spread over the
 // first four step pairs: issued all at once, the 24 loads of every wave
 // backed up in the texture unit and stalled the waves' MFMA issue (about 57
 // cycles per load instruction, by counters).
@@ -401,10 +399,8 @@ __device__ __forceinline__ void m32_issue_part(const GemmArgs& g, int64_t m0, in
     __builtin_amdgcn_global_load_lds((glb_void_t*)(b0 + boff), (lds_void_t*)(buf + L::kOffB + 1024 * bb), 16,
                                      0, 0);
   }
-  if (U < 4)
-    m32_issue_scale_slot<4, U>(g.a_scales + m0 * ks + k0 / 16, ks, buf + L::kOffAS);
-  else if (U < 4 + NT)
-    m32_issue_scale_slot<NT, U - 4>(g.b_scales + n0 * ks + k0 / 16, ks, buf + L::kOffBS);
+  if (U == 0) m32_issue_scales<256>(g.a_scales + m0 * ks + k0 / 16, ks, buf + L::kOffAS);
+  if (U == 1) m32_issue_scales<64 * NT>(g.b_scales + n0 * ks + k0 / 16, ks, buf + L::kOffBS);
 }
 
 template <int NT>
@@ -424,12 +420,20 @@ template <int NT>
 __device__ __forceinline__ void m32_read_scales(const uint8_t* buf, int wm, int wn, int r, int gq,
                                                 M32Scales<NT>& d) {
   using L = M32<NT>;
-  const uint4* pa = reinterpret_cast<const uint4*>(buf + L::kOffAS + 32 * ((2 * gq + wm) * 32 + r));
-  const uint4* pb = reinterpret_cast<const uint4*>(buf + L::kOffBS + 8 * NT * ((2 * gq + wn) * 32 + r));
-  d.a[0] = pa[0];
-  d.a[1] = pa[1];
+  // tile-row i of A is row wm * 128 + 32 i + r; lane group gq takes blocks
+  // 8 gq .. 8 gq + 7, i.e. bytes 8 gq .. 8 gq + 7 of the row (a read
+  // instruction covers 512 contiguous bytes: no bank conflicts)
+  const uint8_t* pa = buf + L::kOffAS + 16 * (wm * 128 + r) + 8 * gq;
+  const uint8_t* pb = buf + L::kOffBS + 16 * (wn * 32 * NT + r) + 8 * gq;
+  uint2 ra[4], rb[NT];
 #pragma unroll
-  for (int k = 0; k < (NT + 1) / 2; ++k) d.b[k] = pb[k];
+  for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const uint2*>(pa + 16 * 32 * i);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) rb[j] = *reinterpret_cast<const uint2*>(pb + 16 * 32 * j);
+  d.a[0] = make_uint4(ra[0].x, ra[0].y, ra[1].x, ra[1].y);
+  d.a[1] = make_uint4(ra[2].x, ra[2].y, ra[3].x, ra[3].y);
+#pragma unroll
+  for (int k = 0; k < (NT + 1) / 2; ++k) d.b[k] = make_uint4(rb[2 * k].x, rb[2 * k].y, rb[2 * k + 1].x, rb[2 * k + 1].y);
 }
 
 // raw codes of blocks 8g + 2Q and 8g + 2Q + 1 (one 16-byte chunk) for the
@@ -805,7 +809,7 @@ void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
                        ((uintptr_t)g.b_codes % 16 == 0) && ((uintptr_t)g.a_scales % 8 == 0) &&
                        ((uintptr_t)g.b_scales % 8 == 0);
   if (aligned && g.M % 256 == 0 && g.N % 256 == 0 && g.K % (2 * kDirBK) == 0 &&
-      g.K <= (INT64_C(1) << 24) && (uintptr_t)g.a_scales % 4 == 0 && (uintptr_t)g.b_scales % 4 == 0) {
+      g.K <= (INT64_C(1) << 24) && (uintptr_t)g.a_scales % 16 == 0 && (uintptr_t)g.b_scales % 16 == 0) {
     // (K <= 2^24 keeps the 32-bit byte offsets of m32_issue, up to 255 rows
     // of K / 2 bytes, below 2^31)
     const int64_t ntiles = (g.M / 256) * (g.N / 256);

@@ -177,7 +177,8 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
  * bytes are those the quantizers produce (0x00 .. 0x7E); the kernels read
  * the low seven bits of a byte.
  * Shapes: M, N >= 1, K >= 16, K % 16 == 0.  Alignment: codes 8 bytes, C 4
- * bytes (16-byte codes, 8-byte scales and K % 128 == 0 take the fast path).
+ * bytes (16-byte aligned codes and scales, M and N multiples of 256 and
+ * K % 512 == 0 take the fast path).
  */
 int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale,
