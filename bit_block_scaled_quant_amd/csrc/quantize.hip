@@ -17,10 +17,10 @@
 //   k_encode_ct     1x16 rowwise blocks plus the columnwise copy (blocks of
 //                   16 rows, written as rows of the transpose), described
 //                   with the cast-transpose below;
-//   k_encode_2d     16x16 blocks (2B.3): one wave per 16 x 64 strip, one
-//                   scale per block, each element encoded once and written
-//                   both ways, so the transposed copy is bit-identical to
-//                   quantizing W^T.
+//   k_encode_ct<.., TWO_D>  16x16 blocks (2B.3) in the cast-transpose
+//                   tiles: one scale per block, each element encoded once
+//                   and written both ways, so the transposed copy is the
+//                   transpose of the codes and scales.
 // The cast-transpose (k_amax_ct, k_encode_ct) makes the rowwise copy and an
 // independently scaled columnwise copy (with the transform along columns)
 // from one read of x per pass.
@@ -231,234 +231,6 @@ __global__ __launch_bounds__(kThreads) void k_encode_rows_blk(const void* __rest
   }
 }
 
-// 2D (16 x 16) blocks: one wave per strip of 16 rows x 64 columns (four
-// blocks side by side); a workgroup covers 128 x 256 (each wave eight strips
-// down its 64 columns), one workgroup per tile.  Each lane loads eight
-// consecutive elements of two rows (rows g and g + 8, eight lanes per row,
-// so loads are 128-byte row segments); a block's 256 elements sit in sixteen
-// lanes, whose amax is a cross-lane reduction, and each lane encodes its own
-// elements (rowwise codes; the scale byte is replicated on every row of the
-// block).  The transposed copy is those codes transposed: the strip's
-// codes go through 512 bytes of LDS and every lane transposes one 8 x 8
-// nibble tile, so SR codes use the rowwise draws (element r * C + c,
-// stream 0) in both copies and the copy is bit-identical to quantizing W^T.
-constexpr int kStripCols = 64;
-
-// r[i] holds nibbles (i, 0..7) of an 8 x 8 nibble matrix; afterwards r[j]
-// holds nibbles (0..7, j): 16-bit, 8-bit, then 4-bit block swaps
-__device__ __forceinline__ void nib_transpose8(uint32_t r[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t a = r[i], b = r[i + 4];
-    r[i] = (a & 0x0000FFFFu) | (b << 16);
-    r[i + 4] = (a >> 16) | (b & 0xFFFF0000u);
-  }
-#pragma unroll
-  for (int h = 0; h < 8; h += 4)
-#pragma unroll
-    for (int i = h; i < h + 2; ++i) {
-      const uint32_t a = r[i], b = r[i + 2];
-      r[i] = (a & 0x00FF00FFu) | ((b & 0x00FF00FFu) << 8);
-      r[i + 2] = ((a >> 8) & 0x00FF00FFu) | (b & 0xFF00FF00u);
-    }
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const uint32_t a = r[i], b = r[i + 1];
-    r[i] = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
-    r[i + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
-  }
-}
-
-// max over the sixteen lanes of a DPP row (quad swaps, then rotations by 4
-// and 8 within the row)
-__device__ __forceinline__ float row16_max(float m) {
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x124, 0xF, 0xF, true)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, true)));
-  return m;
-}
-
-// STAGED (whole tiles: C % 256 == 0, R % 128 == 0, 16-byte aligned outputs):
-// the tile's rowwise codes and row scales are gathered in LDS and leave after
-// one barrier as 16-byte stores, eight lanes per 128-byte row line; the
-// transposed codes leave as four 16-byte pieces per 64-byte column line.
-// Scattered small stores otherwise keep the L1's outstanding requests full
-// (measured: 7.4M write requests of 16 bytes for the 20480 x 5120 weight).
-// Otherwise every strip stores its own pieces directly.
-template <bool BF16, bool SR, bool STAGED>
-__global__ __launch_bounds__(kThreads) void k_encode_2d(
-    const void* __restrict__ x, int64_t R, int64_t C, uint64_t seed, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t,
-    float* __restrict__ ts) {
-  // per wave: one strip's codes [row][8-column chunk], the tile's transposed
-  // codes [column][row / 8] and one strip's row scale words; per workgroup
-  // (STAGED): the tile's codes [row][32 words] and row scales [row][4 words]
-  __shared__ uint32_t qs_all[kThreads / 64][16 * 8];
-  __shared__ uint32_t tq_all[kThreads / 64][64 * 16];
-  __shared__ uint32_t rs_all[kThreads / 64][16];
-  __shared__ __align__(16) uint32_t cq[STAGED ? 128 * 32 : 1];
-  __shared__ __align__(16) uint32_t sq[STAGED ? 128 * 4 : 1];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint32_t* qs = qs_all[wv];
-  uint32_t* tq = tq_all[wv];
-  uint8_t* rs = reinterpret_cast<uint8_t*>(rs_all[wv]);
-  __shared__ float inv_tab[kInvTable];
-  const float s_enc = tensor_scale_from_amax(ts[1]);
-  if (blockIdx.x == 0 && threadIdx.x == 0) ts[0] = s_enc;
-  build_inv_table(inv_tab, s_enc);
-  const int64_t tiles_c = (C + 4 * kStripCols - 1) / (4 * kStripCols);
-  const int64_t ntiles = ((R + 127) / 128) * tiles_c;
-  // Workgroups are dealt to the eight XCDs in turn; tile numbers are laid
-  // out so that each XCD takes a contiguous run of tiles in column-major
-  // order: the tiles that complete one line of the transposed codes (64
-  // bytes each) and of the transposed scales (8 bytes each) are then
-  // neighbours in one L2 (column-major instead of row-major: W's writes
-  // 143.6 -> 126.9 MB for 118 MB of output, the cold-cache 2D calls 3-6%
-  // faster).
-  const int64_t per_xcd = (ntiles + 7) / 8;
-  const int64_t tile = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (tile >= ntiles) return;
-  // load/encode role: block b = lane / 16 (the lane's DPP row), rows g and
-  // g + 8 of the strip, column half hf; one load instruction covers eight
-  // whole 128-byte row segments
-  const int b = lane >> 4, g = (lane >> 1) & 7, hf = lane & 1, c = 2 * b + hf;
-  // transposition role: block, row half, column half, column pair
-  const int rh = (lane >> 3) & 1, ch = (lane >> 2) & 1, jq = lane & 3;
-  // a workgroup tile is 128 rows x 256 columns; wave wv walks down its
-  // 64-column strip
-  const int64_t tiles_r = (R + 127) / 128;
-  const int64_t tc0 = (tile / tiles_r) * (4 * kStripCols);
-  const int64_t c0 = tc0 + wv * kStripCols;
-  const int64_t rt = (tile % tiles_r) * 128;
-  if (!STAGED && c0 >= C) return;
-  const int64_t col = c0 + 8 * c;
-  const bool act = STAGED || col < C;  // C % 16 == 0: both halves of a block agree
-  const int nstrips = STAGED ? 8 : (int)min<int64_t>(8, (R - rt) / 16);
-  uint32_t st_lo = 0u, st_hi = 0u;  // transposed scale bytes of column c0 + lane
-  // All of the tile's loads go out first (bf16: 64 VGPRs of raw data), so a
-  // wave has eight strips of reads in flight; fp32 input keeps two.
-  constexpr int kAhead = BF16 ? 8 : 2;
-  Raw8<BF16> ra[kAhead], rb[kAhead];
-  const int64_t e0 = (rt + g) * C + col;
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i)
-    if (act && i < nstrips) {
-      ra[i] = load8_raw<BF16>(x, e0 + 16 * i * C);
-      rb[i] = load8_raw<BF16>(x, e0 + (16 * i + 8) * C);
-    }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i >= nstrips) break;
-    const int64_t r0 = rt + i * 16;
-    const int64_t ea = e0 + 16 * i * C, eb = ea + 8 * C;
-    float va[8], vb[8];
-    unpack8<BF16>(ra[i % kAhead], va);
-    unpack8<BF16>(rb[i % kAhead], vb);
-    if (kAhead < 8 && act && i + kAhead < nstrips) {
-      ra[i % kAhead] = load8_raw<BF16>(x, ea + 16 * kAhead * C);
-      rb[i % kAhead] = load8_raw<BF16>(x, eb + 16 * kAhead * C);
-    }
-    float m = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fmaxf(fabsf(va[j]), fabsf(vb[j])));
-    m = row16_max(m);
-    float inv;
-    const uint32_t byte = block_scale(m, s_enc, inv_tab, &inv);
-    uint32_t qa = 0u, qb = 0u;
-    if (act) {
-      qa = encode8<SR>(va, inv, seed, 0u, (uint64_t)ea);
-      qb = encode8<SR>(vb, inv, seed, 0u, (uint64_t)eb);
-    }
-    if (STAGED) {
-      cq[(i * 16 + g) * 32 + wv * 8 + c] = qa;
-      cq[(i * 16 + g + 8) * 32 + wv * 8 + c] = qb;
-      if (hf == 0) {
-        uint8_t* sb = reinterpret_cast<uint8_t*>(sq);
-        sb[(i * 16 + g) * 16 + wv * 4 + b] = (uint8_t)byte;
-        sb[(i * 16 + g + 8) * 16 + wv * 4 + b] = (uint8_t)byte;
-      }
-    } else if (act) {
-      *reinterpret_cast<uint32_t*>(codes + ea / 2) = qa;
-      *reinterpret_cast<uint32_t*>(codes + eb / 2) = qb;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    // row scales: byte b of word r is block b's scale (every row of a block)
-    if (!STAGED && hf == 0) {
-      rs[g * 4 + b] = (uint8_t)byte;
-      rs[(g + 8) * 4 + b] = (uint8_t)byte;
-    }
-    if (codes_t) {
-      qs[g * 8 + c] = qa;
-      qs[(g + 8) * 8 + c] = qb;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    if (!STAGED && lane < 16) {
-      // the strip's row scales: four blocks per row, fewer at a ragged edge
-      const int64_t rw = (r0 + lane) * (C / 16) + c0 / 16;
-      const uint32_t wsc = rs_all[wv][lane];
-      if ((C & 63) == 0 && ((uintptr_t)scales & 3) == 0) {
-        *reinterpret_cast<uint32_t*>(scales + rw) = wsc;  // 4-byte aligned
-      } else {
-        for (int k = 0; k < 4 && c0 + 16 * k < C; ++k) scales[rw + k] = (uint8_t)(wsc >> (8 * k));
-      }
-    }
-    if (codes_t) {
-      uint32_t t[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) t[k] = qs[(rh * 8 + k) * 8 + 2 * b + ch];
-      nib_transpose8(t);
-      // columns 16 b + 8 ch + 2 jq and the next one of the strip; rows
-      // r0 + 8 rh .. + 7, i.e. word 2 i + rh of the column's 128 rows
-      const uint32_t w0 = jq == 0 ? t[0] : jq == 1 ? t[2] : jq == 2 ? t[4] : t[6];
-      const uint32_t w1 = jq == 0 ? t[1] : jq == 1 ? t[3] : jq == 2 ? t[5] : t[7];
-      const int cl = 16 * b + 8 * ch + 2 * jq;
-      tq[cl * 16 + 2 * i + rh] = w0;
-      tq[(cl + 1) * 16 + 2 * i + rh] = w1;
-      // lane l: column c0 + l, in this lane's block b = l / 16
-      if (i < 4) st_lo |= byte << (8 * i);
-      else st_hi |= byte << (8 * (i - 4));
-    }
-  }
-  if (STAGED) {
-    __syncthreads();
-    // rowwise codes: 128 rows x 128 bytes, eight lanes per row line
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int id = threadIdx.x + kThreads * k, row = id >> 3, part = id & 7;
-      *reinterpret_cast<uint4*>(codes + (rt + row) * (C / 2) + tc0 / 2 + 16 * part) =
-          *reinterpret_cast<const uint4*>(cq + row * 32 + 4 * part);
-    }
-    if (threadIdx.x < 128)  // row scales: 16 blocks per row
-      *reinterpret_cast<uint4*>(scales + (rt + threadIdx.x) * (C / 16) + tc0 / 16) =
-          *reinterpret_cast<const uint4*>(sq + threadIdx.x * 4);
-    if (!codes_t) return;
-    // transposed codes: the wave's 64 columns, four lanes per 64-byte line
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int cl = 16 * k + (lane >> 2), p = lane & 3;
-      *reinterpret_cast<uint4*>(codes_t + (c0 + cl) * (R / 2) + rt / 2 + 16 * p) =
-          *reinterpret_cast<const uint4*>(tq + cl * 16 + 4 * p);
-    }
-    *reinterpret_cast<uint2*>(scales_t + (c0 + lane) * (R / 16) + rt / 16) = make_uint2(st_lo, st_hi);
-    return;
-  }
-  if (!codes_t || c0 + lane >= C) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  // column c0 + lane of the transposed copy: 8 bytes of codes per strip, the
-  // whole 64-byte line for a full tile
-  uint8_t* dct = codes_t + (c0 + lane) * (R / 2) + rt / 2;
-  const uint32_t* src = tq + lane * 16;
-  for (int i = 0; i < nstrips; ++i)
-    *reinterpret_cast<uint2*>(dct + 8 * i) = make_uint2(src[2 * i], src[2 * i + 1]);
-  uint8_t* dst = scales_t + (c0 + lane) * (R / 16) + rt / 16;
-  if (nstrips == 8 && (R / 16) % 8 == 0 && ((uintptr_t)scales_t & 7) == 0) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(st_lo, st_hi);
-  } else {
-    for (int i = 0; i < nstrips; ++i) dst[i] = (uint8_t)((i < 4 ? st_lo >> (8 * i) : st_hi >> (8 * (i - 4))));
-  }
-}
-
 // ----------------------------------------------------- cast-transpose ----
 // Both operands a training step takes from one tensor x [R][C], read in its
 // own layout: the rowwise copy (1x16 blocks along rows, as nvfp4_quantize
@@ -542,6 +314,59 @@ __device__ __forceinline__ float chunk_elem(const Chunk16<BF16>& ch, int j, int 
   const uint32_t w = wi == 0 ? q.x : wi == 1 ? q.y : wi == 2 ? q.z : q.w;
   if (BF16) return __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
   return __uint_as_float(w);
+}
+
+// r[i] holds nibbles (i, 0..7) of an 8 x 8 nibble matrix; afterwards r[j]
+// holds nibbles (0..7, j): 16-bit, 8-bit, then 4-bit block swaps
+__device__ __forceinline__ void nib_transpose8(uint32_t r[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = r[i], b = r[i + 4];
+    r[i] = (a & 0x0000FFFFu) | (b << 16);
+    r[i + 4] = (a >> 16) | (b & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int h = 0; h < 8; h += 4)
+#pragma unroll
+    for (int i = h; i < h + 2; ++i) {
+      const uint32_t a = r[i], b = r[i + 2];
+      r[i] = (a & 0x00FF00FFu) | ((b & 0x00FF00FFu) << 8);
+      r[i + 2] = ((a >> 8) & 0x00FF00FFu) | (b & 0xFF00FF00u);
+    }
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t a = r[i], b = r[i + 1];
+    r[i] = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
+    r[i + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  }
+}
+
+// max |x| over a lane's 16 x 8 elements of a chunk: integer max of the
+// magnitudes' bit patterns (order-preserving for non-negative floats), two
+// bf16 per word
+template <bool BF16>
+__device__ __forceinline__ float chunk_absmax(const Chunk16<BF16>& ch) {
+  if (BF16) {
+    ushort2v m = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint4& q = ch.w[j][0];
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2v, q.x & 0x7FFF7FFFu));
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2v, q.y & 0x7FFF7FFFu));
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2v, q.z & 0x7FFF7FFFu));
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2v, q.w & 0x7FFF7FFFu));
+    }
+    return __uint_as_float((uint32_t)max(m.x, m.y) << 16);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int h = 0; h < (BF16 ? 1 : 2); ++h) {
+      const uint4& q = ch.w[j][h];
+      m = max(m, max(max(q.x & 0x7FFFFFFFu, q.y & 0x7FFFFFFFu), max(q.z & 0x7FFFFFFFu, q.w & 0x7FFFFFFFu)));
+    }
+  return __uint_as_float(m);
 }
 
 // block_max_to for two maxima: m into ts[1], mt into ts_t[1]
@@ -672,7 +497,17 @@ __global__ __launch_bounds__(kThreads) void k_amax_ct(const void* __restrict__ x
 // back (measured 30% slower).  fp32 input holds twice the register data and
 // spilled 57-94 VGPRs under that bound; with two waves per SIMD it takes
 // 149-195 without spills and runs 10-22% faster (measured).
-template <bool BF16, bool SR, bool RHT>
+//
+// TWO_D: the same tiles and write-out for the 16x16 blocks of 2B.3 (no
+// transform; ts_t is ts; codes_t may be null).  A block is the 16 x 8
+// elements of a lane pair, so its maximum is the lanes' own maxima met by
+// one DPP swap; each element is encoded once (SR: the rowwise draws, element
+// r * C + c, stream 0), and the transposed codes of a lane are the nibble
+// transpose of its sixteen row words, in registers.  (This replaced a
+// 16 x 64-strip kernel that moved the codes through LDS for the transpose:
+// W [20480 x 5120] took 66 us there, at 11 VALU instructions per element
+// and LDS bank-conflict cycles five times its LDS-active cycles.)
+template <bool BF16, bool SR, bool RHT, bool TWO_D = false>
 __global__ __launch_bounds__(kCtThreads, BF16 ? 4 : 2) void k_encode_ct(
     const void* __restrict__ x, int64_t R, int64_t C, uint64_t seed, uint64_t seed_t, uint32_t stream_t,
     uint32_t rht_mask,
@@ -718,7 +553,42 @@ __global__ __launch_bounds__(kCtThreads, BF16 ? 4 : 2) void k_encode_ct(
   const bool stage = nch == kCtChunks && ncols == kCtCols && (C / 2) % 16 == 0 &&
                      ((uintptr_t)codes & 15) == 0;  // workgroup-uniform
 
-  if (wv < nch) {  // wave-uniform: every lane of the wave takes part below
+  if (TWO_D && wv < nch) {  // wave-uniform
+    Chunk16<BF16> ch;
+    if (lane_ok)
+      load_chunk<BF16>(x, r0 * C + c0 + cl, C, ch);
+    else
+      zero_chunk<BF16>(ch);
+    float m = chunk_absmax<BF16>(ch);
+    m = fmaxf(m, lane_pair_swap(m));
+    float inv;
+    const uint32_t byte = block_scale(m, s_enc, inv_tab[0], &inv);
+    uint32_t w[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = chunk_elem<BF16>(ch, j, k);
+      const int64_t e = (r0 + j) * C + c0 + cl;
+      w[j] = encode8<SR>(v, inv, seed, 0u, (uint64_t)e);
+      if (stage)
+        rq[16 * wv + j][lane] = w[j];
+      else if (lane_ok)
+        *reinterpret_cast<uint32_t*>(codes + e / 2) = w[j];
+      if (!(lane & 1)) rs[16 * wv + j][lane >> 1] = (uint8_t)byte;
+    }
+    if (codes_t) {
+      nib_transpose8(w);
+      nib_transpose8(w + 8);
+      uint8_t* tqw = tq + wv * kPitch + 64 * lane;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        *reinterpret_cast<uint2*>(tqw + 8 * (k ^ (lane & 7))) = make_uint2(w[k], w[8 + k]);
+      const uint32_t b4 = byte * 0x01010101u;
+      *reinterpret_cast<uint2*>(&cs[wv][cl]) = make_uint2(b4, b4);
+    }
+  }
+  if (!TWO_D && wv < nch) {  // wave-uniform: every lane of the wave takes part below
     Chunk16<BF16> ch;
     if (lane_ok)
       load_chunk<BF16>(x, r0 * C + c0 + cl, C, ch);
@@ -796,6 +666,7 @@ __global__ __launch_bounds__(kCtThreads, BF16 ? 4 : 2) void k_encode_ct(
       scales[(rt + row) * srow + c0 / 16 + b] = rs[row][b];
     }
   }
+  if (TWO_D && !codes_t) return;
   // columnwise codes: four threads per column, 16 bytes (two chunks) each
   const int64_t tpitch = R / 2;
   const bool t16 = tpitch % 16 == 0 && ((uintptr_t)codes_t & 15) == 0;
@@ -885,23 +756,18 @@ static void launch_rows(const QuantArgs& a, int cus, hipStream_t st) {
                        a.tensor_scale);
 }
 
-template <bool BF16, bool SR, bool RHT>
+template <bool BF16, bool SR, bool RHT, bool TWO_D = false>
 static void launch_ct_encode(const CastTransposeArgs& a, int cus, hipStream_t st);
 
 template <bool BF16, bool SR>
 static void launch_tile(const QuantArgs& a, bool two_d, int cus, hipStream_t st) {
   if (two_d) {
-    const int64_t tiles = ((a.rows + 127) / 128) * ((a.cols + 4 * kStripCols - 1) / (4 * kStripCols));
-    const int blocks = (int)(((tiles + 7) / 8) * 8);  // tiles <= 2^25 (rows * cols <= 2^40)
-    const bool staged = a.cols % 256 == 0 && a.rows % 128 == 0 && (uintptr_t)a.codes % 16 == 0 &&
-                        (uintptr_t)a.scales % 16 == 0 &&
-                        (!a.codes_t || ((uintptr_t)a.codes_t % 16 == 0 && (uintptr_t)a.scales_t % 8 == 0));
-    if (staged)
-      hipLaunchKernelGGL((k_encode_2d<BF16, SR, true>), dim3(blocks), dim3(kThreads), 0, st, a.x, a.rows,
-                         a.cols, a.seed, a.codes, a.scales, a.codes_t, a.scales_t, a.tensor_scale);
-    else
-      hipLaunchKernelGGL((k_encode_2d<BF16, SR, false>), dim3(blocks), dim3(kThreads), 0, st, a.x, a.rows,
-                         a.cols, a.seed, a.codes, a.scales, a.codes_t, a.scales_t, a.tensor_scale);
+    // the cast-transpose encoder in its 16x16-block mode: one tensor scale,
+    // every element encoded once from the rowwise draws
+    CastTransposeArgs c{a.x,     a.bf16,   a.rows,         a.cols,  a.rounding, a.seed, a.seed,
+                        false,   0u,       a.codes,        a.scales, a.tensor_scale, a.codes_t, a.scales_t,
+                        a.tensor_scale, 0u};
+    launch_ct_encode<BF16, SR, false, true>(c, cus, st);
   } else {
     // 1D with the columnwise copy: the cast-transpose encoder with one tensor
     // scale for both copies and the columnwise SR draws from stream 1 of seed
@@ -947,11 +813,11 @@ void launch_quantize(const QuantArgs& a, int cus, hipStream_t st) {
     launch_quantize_t<false>(a, cus, st);
 }
 
-template <bool BF16, bool SR, bool RHT>
+template <bool BF16, bool SR, bool RHT, bool TWO_D>
 static void launch_ct_encode(const CastTransposeArgs& a, int, hipStream_t st) {
   const int64_t tiles = ((a.rows + 127) / 128) * ((a.cols + kCtCols - 1) / kCtCols);
   const int blocks = (int)(((tiles + 7) / 8) * 8);  // tiles <= 2^24 (rows * cols <= 2^40)
-  hipLaunchKernelGGL((k_encode_ct<BF16, SR, RHT>), dim3(blocks), dim3(kCtThreads), 0, st, a.x, a.rows, a.cols,
+  hipLaunchKernelGGL((k_encode_ct<BF16, SR, RHT, TWO_D>), dim3(blocks), dim3(kCtThreads), 0, st, a.x, a.rows, a.cols,
                      a.seed, a.seed_t, a.stream_t, a.rht_mask, a.codes, a.scales, a.tensor_scale, a.codes_t,
                      a.scales_t, a.tensor_scale_t);
 }
