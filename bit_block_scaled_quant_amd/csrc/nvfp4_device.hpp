@@ -294,14 +294,41 @@ __device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float v[8]) {
   }
 }
 
-// max |v| as a tree (independent max3 chains rather than one serial chain)
-__device__ __forceinline__ float max_abs8(const float v[8]) {
-  const float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
-  const float b = fmaxf(fmaxf(fabsf(v[3]), fabsf(v[4])), fabsf(v[5]));
-  return fmaxf(fmaxf(a, b), fmaxf(fabsf(v[6]), fabsf(v[7])));
+// max(|a|, |b|, |c|) in one v_max3_f32 with absolute-value modifiers.
+// Inputs are finite (the calls' contract), so the NaN-quieting moves the
+// compiler puts before fmaxf of values it cannot prove canonical are not
+// needed.
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
-__device__ __forceinline__ float max_abs16(const float v[16]) { return fmaxf(max_abs8(v), max_abs8(v + 8)); }
+// max of two non-negative floats as an integer max of their bit patterns
+__device__ __forceinline__ float max_nonneg(float a, float b) {
+  return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
+}
+
+// max |v| as a tree (independent max3 chains rather than one serial chain)
+__device__ __forceinline__ float max_abs8(const float v[8]) {
+  const float a = max3_abs(v[0], v[1], v[2]);
+  const float b = max3_abs(v[3], v[4], v[5]);
+  return max_nonneg(b, max3_abs(v[6], v[7], a));
+}
+
+__device__ __forceinline__ float max_abs16(const float v[16]) {
+  const float a = max3_abs(v[0], v[1], v[2]), b = max3_abs(v[3], v[4], v[5]), c = max3_abs(v[6], v[7], v[8]);
+  const float d = max3_abs(v[9], v[10], v[11]), e = max3_abs(v[12], v[13], v[14]);
+  return max_nonneg(max3_abs(a, b, v[15]), max3_abs(c, d, e));
+}
+
+// the maximum of a non-negative value and its neighbour's in the lane pair
+// (2k, 2k + 1): one integer max with a DPP quad swap
+__device__ __forceinline__ float pair_max(float m) {
+  const uint32_t b = __float_as_uint(m);
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0xB1, 0xF, 0xF, true);
+  return __uint_as_float(max(b, o));
+}
 
 // E2M1 magnitude of index m (0..7): 0, 0.5, 1, 1.5, 2, 3, 4, 6
 __device__ __forceinline__ float e2m1_magnitude(uint32_t m) {
@@ -328,7 +355,10 @@ __device__ __forceinline__ float amax16(const float v[16]) {
 // is round-to-nearest-even onto the E2M1 grid for every fp32 input (ties to the even code, saturation at 6,
 // sign kept); the exhaustive device test checks that against the oracle.
 __device__ __forceinline__ uint32_t e2m1_rne8(const float* y) {
-  uint32_t w = 0;
+  // the four conversions write all four bytes: the word starts as whatever
+  // its register holds (an empty asm defines it without an instruction)
+  uint32_t w;
+  asm("" : "=v"(w));
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_rows(const void* __restrict
       float m = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
-      m = fmaxf(m, lane_pair_swap(m));
+      m = pair_max(m);
       float inv;
       const uint32_t byte = block_scale(m, s_enc, inv_tab, &inv);
       if (valid[u]) {
@@ -520,11 +520,21 @@ __global__ __launch_bounds__(kCtThreads, BF16 ? 4 : 2) void k_encode_ct(
   // k ^ (l & 7) (the xor spreads a store instruction over the banks); 16
   // bytes of padding per chunk row spread the write-out reads
   constexpr int kPitch = kCtCols * 8 + 16;
-  __shared__ float inv_tab[2][kInvTable];
-  __shared__ __align__(16) uint8_t tq[kCtChunks * kPitch];
-  __shared__ __align__(16) uint8_t cs[kCtChunks][kCtCols];           // columnwise scales
-  __shared__ __align__(16) uint8_t rs[kCtChunks * 16][kCtCols / 16];  // rowwise scales
-  __shared__ __align__(16) uint32_t rq[kCtChunks * 16][kCtCols / 8];  // rowwise codes (whole tiles)
+  // One LDS block with the inverse-scale tables first: at offset 0 a
+  // block's multiplier is a read at (byte << 2) with no base register.
+  struct Smem {
+    float inv_tab[2][kInvTable];
+    __align__(16) uint8_t tq[kCtChunks * kPitch];
+    __align__(16) uint8_t cs[kCtChunks][kCtCols];           // columnwise scales
+    __align__(16) uint8_t rs[kCtChunks * 16][kCtCols / 16];  // rowwise scales
+    __align__(16) uint32_t rq[kCtChunks * 16][kCtCols / 8];  // rowwise codes (whole tiles)
+  };
+  __shared__ Smem sm;
+  auto& inv_tab = sm.inv_tab;
+  auto& tq = sm.tq;
+  auto& cs = sm.cs;
+  auto& rs = sm.rs;
+  auto& rq = sm.rq;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float amax = ts[1];
   const float amax_t = RHT ? ts_t[1] : amax;
@@ -560,7 +570,7 @@ __global__ __launch_bounds__(kCtThreads, BF16 ? 4 : 2) void k_encode_ct(
     else
       zero_chunk<BF16>(ch);
     float m = chunk_absmax<BF16>(ch);
-    m = fmaxf(m, lane_pair_swap(m));
+    m = pair_max(m);
     float inv;
     const uint32_t byte = block_scale(m, s_enc, inv_tab[0], &inv);
     uint32_t w[16];
@@ -602,7 +612,7 @@ __global__ __launch_bounds__(kCtThreads, BF16 ? 4 : 2) void k_encode_ct(
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = chunk_elem<BF16>(ch, j, k);
       float m = max_abs8(v);
-      m = fmaxf(m, lane_pair_swap(m));
+      m = pair_max(m);
       float inv;
       const uint32_t byte = block_scale(m, s_enc, inv_tab[0], &inv);
       const int64_t e = (r0 + j) * C + c0 + cl;
