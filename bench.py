@@ -99,6 +99,22 @@ def traffic_record(kernel_src):
     return rec
 
 
+def quant_traffic_record():
+    """HBM bytes of the step's quantizer calls measured by rocprofv3 counters
+    (FETCH_SIZE, WRITE_SIZE, scaled by a plain copy's reading), valid only for
+    the sources they were taken with."""
+    path = os.path.join(ROOT, "profiles", "quant_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for src in rec.get("sources", []):
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec
+
+
 def cpu_baseline():
     """The oracle, as it stands, on a bounded sample of the same step; its
     per-element / per-output rates are scaled to the full step."""
@@ -542,6 +558,8 @@ def main():
     components = {}
     gemm_ms = []
     quant_ms_total, quant_bytes_total = 0.0, 0.0
+    qrec = quant_traffic_record()
+    quant_counter_bytes = 0.0 if qrec else None
     for name, kind, _, meta in calls:
         ms = float(np.median(per_call[name]))
         if kind == "gemm":
@@ -560,6 +578,16 @@ def main():
                                 "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                                 "frac_hbm_peak_one_read_bound": round(
                                     meta["one_read"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            # the HBM bytes the counters saw for this call (profiles/quant_traffic.json)
+            c = qrec["calls"].get(name) if qrec else None
+            if c is not None:
+                cb = c["read_bytes"] + c["write_bytes"]
+                quant_counter_bytes += cb
+                components[name]["counter_bytes"] = cb
+                components[name]["frac_hbm_peak_counters"] = round(cb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            elif qrec is not None:
+                quant_counter_bytes = None
+                qrec = None
 
     avg_gemm_ms = float(np.mean(gemm_ms))
     achieved = gemm_flops / (avg_gemm_ms * 1e-3) / 1e12
@@ -595,6 +623,11 @@ def main():
         "quantize_GBps": round(quant_bytes_total / (quant_ms_total * 1e-3) / 1e9, 1),
         "quantize_frac_hbm_peak": round(quant_bytes_total / (quant_ms_total * 1e-3) / 1e9
                                         / HBM_PEAK_GBS, 4),
+        # the same time against the HBM bytes the counters measured for these
+        # calls (null when the quantizer sources changed since they were taken)
+        "quantize_frac_hbm_peak_counters": (round(quant_counter_bytes / (quant_ms_total * 1e-3) / 1e9
+                                                  / HBM_PEAK_GBS, 4)
+                                            if quant_counter_bytes is not None else None),
         "components": components,
         "extras": extras,
         "roofline": roofline,
