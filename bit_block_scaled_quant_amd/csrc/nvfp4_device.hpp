@@ -170,6 +170,32 @@ __device__ __forceinline__ void hadamard16(float v[16]) {
   }
 }
 
+// max_j |(H16 v)_j| for the amax pass.  The last stage (h = 8) turns the pair
+// a = v[j], b = v[j + 8] into a + b and a - b, and max(|fl(a + b)|,
+// |fl(a - b)|) = fl(|a| + |b|) exactly: one of the two is a sum of the
+// magnitudes, the other a difference no larger, and rounding is symmetric
+// and monotone.  So that stage and the maxima over its 16 outputs become
+// eight additions of magnitudes and a maximum over eight, with the same
+// result bits.
+__device__ __forceinline__ float hadamard16_absmax(float v[16]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+  uint32_t s[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s[j] = __float_as_uint(__builtin_fabsf(v[j]) + __builtin_fabsf(v[j + 8]));
+  // non-negative floats order like their bit patterns
+  const uint32_t a = max(max(s[0], s[1]), s[2]), b = max(max(s[3], s[4]), s[5]);
+  return __uint_as_float(max(max(a, b), max(s[6], s[7])));
+}
+
 // rht16: v <- 1/4 * H16 * diag(sigma) * v; sign j flips when bit j of mask
 // is set.
 __device__ __forceinline__ void rht16(float v[16], uint32_t mask) {
@@ -214,6 +240,32 @@ __device__ __forceinline__ void rht16_pair(float v[8], uint32_t mask, bool odd) 
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = 0.25f * v[j];
   }
+}
+
+// max_j |(H16 sigma v)_j| over a block held by a lane pair (the transform of
+// rht16_pair without the final 1/4), with the last stage and the maximum
+// merged as in hadamard16_absmax; both lanes of the pair return the block's
+// maximum.
+__device__ __forceinline__ float rht16_pair_absmax(float v[8], uint32_t mask, bool odd) {
+  const uint32_t m8 = odd ? (mask >> 8) : mask;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((m8 >> j) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+  uint32_t s[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    s[j] = __float_as_uint(__builtin_fabsf(lane_pair_swap(v[j])) + __builtin_fabsf(v[j]));
+  const uint32_t a = max(max(s[0], s[1]), s[2]), b = max(max(s[3], s[4]), s[5]);
+  return __uint_as_float(max(max(a, b), max(s[6], s[7])));
 }
 
 // ----------------------------------------------------------- loads -------

@@ -138,9 +138,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_rht(const void* __restrict__ 
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = 0.0f;
       }
-      rht16_pair<false>(v, rht_mask, odd);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+      m = max_nonneg(m, rht16_pair_absmax(v, rht_mask, odd));
     }
   }
   // the transform's final 1/4, applied to the maximum: rounding is monotone,
@@ -468,9 +466,8 @@ __global__ __launch_bounds__(kThreads) void k_amax_ct(const void* __restrict__ x
       float v[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[j] = col4_elem<BF16>(cur, j, k, rht_mask);
-      m = fmaxf(m, max_abs16(v));
-      hadamard16<false>(v);
-      mt = fmaxf(mt, max_abs16(v));
+      m = max_nonneg(m, max_abs16(v));
+      mt = max_nonneg(mt, hadamard16_absmax(v));
     }
     if (more) cur = nxt;
   }
