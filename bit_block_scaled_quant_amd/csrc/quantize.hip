@@ -266,14 +266,6 @@ __device__ __forceinline__ void load_chunk(const void* __restrict__ x, int64_t e
   }
 }
 
-template <bool BF16>
-__device__ __forceinline__ void zero_chunk(Chunk16<BF16>& ch) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-#pragma unroll
-    for (int h = 0; h < (BF16 ? 1 : 2); ++h) ch.w[j][h] = make_uint4(0u, 0u, 0u, 0u);
-}
-
 // The transform's sign flips on the raw storage: row j of a chunk is element
 // j of every columnwise block, so sign j flips all of row j.
 template <bool BF16>
@@ -561,11 +553,15 @@ __global__ __launch_bounds__(kCtThreads, BF16 ? 4 : 2) void k_encode_ct(
                      ((uintptr_t)codes & 15) == 0;  // workgroup-uniform
 
   if (TWO_D && wv < nch) {  // wave-uniform
+    // a lane past the last column loads the last eight columns instead, with
+    // no branch: its values reach only its own blocks (a 16-column block is
+    // a whole lane pair), whose outputs are not stored
     Chunk16<BF16> ch;
-    if (lane_ok)
-      load_chunk<BF16>(x, r0 * C + c0 + cl, C, ch);
-    else
-      zero_chunk<BF16>(ch);
+    load_chunk<BF16>(x, r0 * C + min<int64_t>(c0 + cl, C - 8), C, ch);
+    // all sixteen loads leave before any use: the scheduler would otherwise
+    // start on row 0 after a few of them, and its wait for that row would
+    // hold back the rest for a whole memory latency
+    __builtin_amdgcn_sched_barrier(0);
     float m = chunk_absmax<BF16>(ch);
     m = pair_max(m);
     float inv;
@@ -596,11 +592,15 @@ __global__ __launch_bounds__(kCtThreads, BF16 ? 4 : 2) void k_encode_ct(
     }
   }
   if (!TWO_D && wv < nch) {  // wave-uniform: every lane of the wave takes part below
+    // a lane past the last column loads the last eight columns instead, with
+    // no branch: its values reach only its own blocks (a 16-column block is
+    // a whole lane pair), whose outputs are not stored
     Chunk16<BF16> ch;
-    if (lane_ok)
-      load_chunk<BF16>(x, r0 * C + c0 + cl, C, ch);
-    else
-      zero_chunk<BF16>(ch);
+    load_chunk<BF16>(x, r0 * C + min<int64_t>(c0 + cl, C - 8), C, ch);
+    // all sixteen loads leave before any use: the scheduler would otherwise
+    // start on row 0 after a few of them, and its wait for that row would
+    // hold back the rest for a whole memory latency
+    __builtin_amdgcn_sched_barrier(0);
     const bool odd = lane & 1;
     // rowwise copy: SR stream 0 of seed, element index r * C + c
 #pragma unroll
