@@ -168,11 +168,14 @@ def cpu_baseline():
             "sample": "; ".join(detail) + f"; extrapolated step time {t_total:.1f} s"}
 
 
-def tiny_times(nv, datagen, torch, dev, reps=50):
+def tiny_times(nv, datagen, torch, dev, reps=50, batch=20):
     """The Tiny workload (A, B [256 x 256] fp32, 1% x50 outliers, seed 0, both
-    quantized 1D with RNE, then C = A . B^T): median launch-to-completion
-    time of each call over reps runs, by HIP events on the launch stream.
-    Latency-bound (one or two waves of work), so no roofline claim."""
+    quantized 1D with RNE, then C = A . B^T): device time per call and per
+    pass.  Each call (and the pass) is captured `batch` times back to back in
+    one HIP graph; a replay is timed by HIP events on the replay stream and
+    divided by `batch`, median of `reps` replays.  Timing single eager calls
+    would measure the host's launch latency instead: the GPU idles between
+    them.  Latency-bound (one or two waves of work), so no roofline claim."""
     a = datagen.tiny(dev, seed=0, tag=datagen.TAG_A)
     b = datagen.tiny(dev, seed=0, tag=datagen.TAG_B)
     qa, qb = nv.quantize(a), nv.quantize(b)
@@ -180,29 +183,36 @@ def tiny_times(nv, datagen, torch, dev, reps=50):
     calls = {"quantize_A": lambda: nv.nvfp4_quantize(a, 0, 0, 0, 0, qa.codes, qa.scales, qa.tensor_scale),
              "quantize_B": lambda: nv.nvfp4_quantize(b, 0, 0, 0, 0, qb.codes, qb.scales, qb.tensor_scale),
              "gemm": lambda: nv.gemm(qa, qb, out=c)}
-    out = {}
-    for name, fn in calls.items():
+
+    def timed_graph(fns):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for fn in fns:
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(batch):
+                for fn in fns:
+                    fn()
+        graph.replay()
+        torch.cuda.synchronize()
         ts = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            fn()
+            graph.replay()
             e1.record()
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        out[name + "_us"] = round(float(np.median(ts)), 2)
-    # the whole pass, back to back
-    ts = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for fn in calls.values():
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e3)
-    out["pass_us"] = round(float(np.median(ts)), 2)
+            ts.append(e0.elapsed_time(e1) * 1e3 / batch)
+        return round(float(np.median(ts)), 2)
+
+    out = {name + "_us": timed_graph([fn]) for name, fn in calls.items()}
+    out["pass_us"] = timed_graph(list(calls.values()))
     out["shape"] = "A, B [256 x 256] fp32; C = A . B^T 256 x 256 x 256"
+    out["timing"] = f"HIP graph of {batch} back-to-back calls, median of {reps} replays, per call"
     return out
 
 

@@ -288,21 +288,36 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     __syncthreads();
   }
 
-  // epilogue: C = acc / (S_a * S_b), lane holds rows 4*lg .. 4*lg+3 of column li
+  // epilogue: C = acc / (S_a * S_b), lane holds rows 4*lg .. 4*lg+3 of column li.
+  // The loops are fully unrolled, so every accumulator index is a constant:
+  // a row's offset is formed once per (i, r) and a column's once per j.  With
+  // the 64-bit index of each value formed inside one loop around store_c,
+  // the unrolled body exceeded the compiler's limit, the loop stayed, the
+  // accumulators were indexed at run time and moved to scratch memory (1 KB
+  // per lane), and a 256 x 256 x 256 product took 83 us.
   const float inv_a = __fdiv_rn(1.0f, g.a_ts[0]), inv_b = __fdiv_rn(1.0f, g.b_ts[0]);
   float cmax = 0.0f;
+  const int64_t mrow = m0 + wm * (BM / 2) + lg * 4, ncol = n0 + wn * (BN / 2) + li;
+  auto each = [&](auto&& put) {
 #pragma unroll
-  for (int i = 0; i < TI; ++i) {
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int64_t n = n0 + wn * (BN / 2) + j * 16 + li;
-      if (n >= g.N) continue;
+    for (int i = 0; i < TI; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm * (BM / 2) + i * 16 + lg * 4 + r;
-        if (m < g.M) store_c(g, m * g.N + n, (acc[i][j][r] * inv_a) * inv_b, cmax, false);
+        const int64_t m = mrow + i * 16 + r;
+        const int64_t row = m * g.N + ncol;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          if (m < g.M && ncol + j * 16 < g.N) put(row + j * 16, (acc[i][j][r] * inv_a) * inv_b);
       }
     }
+  };
+  if (!g.c16 && g.beta == 0.0f) {
+    each([&](int64_t idx, float v) {
+      g.c[idx] = v;
+      cmax = fmaxf(cmax, fabsf(v));
+    });
+  } else {
+    each([&](int64_t idx, float v) { store_c(g, idx, v, cmax, false); });
   }
   if (g.amax) amax_to(g, cmax);
 }
