@@ -220,8 +220,24 @@ __device__ __forceinline__ void amax_to(const GemmArgs& g, float m) {
 
 __global__ void k_zero_amax(unsigned* p) { *p = 0u; }
 
+// the T scale bytes (T = 4 or 8) a lane reads for its tiles of one block
+// column, as one 4- or 8-byte LDS read
+template <int T>
+__device__ __forceinline__ void read_scale_bytes(const uint8_t* p, uint32_t w[2]) {
+  static_assert(T == 4 || T == 8, "tiles per wave half");
+  if (T == 8) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+    w[1] = 0u;
+  }
+}
+
 // ---- the kernel ---------------------------------------------------------
-// BM x BN tile per workgroup, (BM/2) x (BN/2) per wave.
+// BM x BN tile per workgroup (256 x 256, or 128 x 128 for problems whose
+// 256 x 256 tiles would not fill the CUs), (BM/2) x (BN/2) per wave.
 template <int BM, int BN, bool ALIGNED>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   constexpr int TI = BM / 32, TJ = BN / 32;  // 16x16 MFMA tiles per wave
@@ -262,14 +278,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // scale bytes of block column 2g + h for all tiles of this lane
       const uint8_t* pa = sm.as + (2 * lg + h) * BM + wm * (BM / 2) + li * TI;
       const uint8_t* pb = sm.bs + (2 * lg + h) * BN + wn * (BN / 2) + li * TJ;
-      uint8_t ba[TI], bb[TJ];
-      *reinterpret_cast<uint2*>(ba) = *reinterpret_cast<const uint2*>(pa);
-      *reinterpret_cast<uint2*>(bb) = *reinterpret_cast<const uint2*>(pb);
+      uint32_t wa[2], wb[2];
+      read_scale_bytes<TI>(pa, wa);
+      read_scale_bytes<TJ>(pb, wb);
       half2v sa[TI], sb[TJ];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) sa[i] = scale_h2(ba[i]);
+      for (int i = 0; i < TI; ++i) sa[i] = scale_h2((uint8_t)(wa[i >> 2] >> (8 * (i & 3))));
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) sb[j] = scale_h2(bb[j]);
+      for (int j = 0; j < TJ; ++j) sb[j] = scale_h2((uint8_t)(wb[j >> 2] >> (8 * (j & 3))));
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         half8 fa[TI], fb[TJ];
@@ -834,10 +850,19 @@ void launch_gemm(const GemmArgs& g, int cus, hipStream_t st) {
       launch_m32<true>(g, ntiles, full, rem, c, st);
     else
       launch_m32<false>(g, ntiles, full, rem, c, st);
-  } else if (aligned) {
-    hipLaunchKernelGGL((k_gemm<BM, BN, true>), grid, dim3(kGemmThreads), 0, st, g);
+  } else if ((int64_t)grid.x * grid.y >= (int64_t)std::max(cus, 1)) {
+    if (aligned)
+      hipLaunchKernelGGL((k_gemm<BM, BN, true>), grid, dim3(kGemmThreads), 0, st, g);
+    else
+      hipLaunchKernelGGL((k_gemm<BM, BN, false>), grid, dim3(kGemmThreads), 0, st, g);
   } else {
-    hipLaunchKernelGGL((k_gemm<BM, BN, false>), grid, dim3(kGemmThreads), 0, st, g);
+    // fewer 256 x 256 tiles than CUs: 128 x 128 tiles, four times as many
+    // workgroups (a 256 x 256 x 256 product: one workgroup 18 us, four 8 us)
+    const dim3 grid128((unsigned)((g.N + 127) / 128), (unsigned)((g.M + 127) / 128));
+    if (aligned)
+      hipLaunchKernelGGL((k_gemm<128, 128, true>), grid128, dim3(kGemmThreads), 0, st, g);
+    else
+      hipLaunchKernelGGL((k_gemm<128, 128, false>), grid128, dim3(kGemmThreads), 0, st, g);
   }
 }
 
