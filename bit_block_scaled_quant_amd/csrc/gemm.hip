@@ -369,11 +369,10 @@ __device__ __forceinline__ int dswz(int r, int c) { return r * kDirRow + ((c ^ (
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // NT = 32-column MFMA tiles per wave along N: 4 for a 256 x 256 workgroup
-// tile, 2 for 256 x 128 (used for the last, partial wave of tiles).
+// tile; 2 (256 x 128) or 1 (256 x 64) for the last, partial wave of tiles.
 template <int NT>
 struct M32 {
   static constexpr int kBN = 64 * NT;                 // tile width
-  static constexpr int kLogNT = NT == 4 ? 2 : 1;
   static constexpr int kOffB = 256 * kDirRow;         // B codes after 32 KB of A codes
   static constexpr int kOffAS = kOffB + kBN * kDirRow;  // A scales, 4 KB
   static constexpr int kOffBS = kOffAS + 4096;          // B scales, NT KB
@@ -464,7 +463,10 @@ __device__ __forceinline__ void m32_read_scales(const uint8_t* buf, int wm, int 
   d.a[0] = make_uint4(ra[0].x, ra[0].y, ra[1].x, ra[1].y);
   d.a[1] = make_uint4(ra[2].x, ra[2].y, ra[3].x, ra[3].y);
 #pragma unroll
-  for (int k = 0; k < (NT + 1) / 2; ++k) d.b[k] = make_uint4(rb[2 * k].x, rb[2 * k].y, rb[2 * k + 1].x, rb[2 * k + 1].y);
+  for (int k = 0; k < (NT + 1) / 2; ++k) {
+    const uint2 hi = 2 * k + 1 < NT ? rb[2 * k + 1 < NT ? 2 * k + 1 : 0] : make_uint2(0u, 0u);
+    d.b[k] = make_uint4(rb[2 * k].x, rb[2 * k].y, hi.x, hi.y);
+  }
 }
 
 // raw codes of blocks 8g + 2Q and 8g + 2Q + 1 (one 16-byte chunk) for the
@@ -622,9 +624,9 @@ __device__ __forceinline__ void m32_stage(const GemmArgs& g, int64_t m0, int64_t
 // A launch covers tiles tile0 .. tile0 + ntl - 1 of that order.  With NT = 4
 // the workgroups are dealt to the eight XCDs in turn and each XCD takes a
 // contiguous run, so its 32 concurrent tiles share 4 slices of A and 8 of B
-// per K-step in its L2 (instead of about 36 distinct ones); with NT = 2 (the
-// last, partial wave) workgroup u computes columns (u % 2) * 128 .. of tile
-// tile0 + u / 2.
+// per K-step in its L2 (instead of about 36 distinct ones); with NT = 2 or 1
+// (the last, partial wave) workgroup u computes columns (u % (4 / NT)) * 64 NT
+// .. of tile tile0 + u / (4 / NT).
 // EX: the epilogue options of nvfp4_gemm_ex (bf16 output, beta, output
 // amax); without them the plain fp32 epilogue, compiled on its own so that
 // the main loop's register allocation is the same as for nvfp4_gemm.
@@ -648,11 +650,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_
     u = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (u >= ntl) return;  // the whole workgroup
   } else {
-    u = blockIdx.x / 2;
+    u = blockIdx.x / (4 / NT);
   }
   int64_t m0, n0;
   tile_mn(tile0 + u, ntm, ntn, m0, n0);
-  if (NT == 2) n0 += (blockIdx.x % 2) * L::kBN;
+  if (NT < 4) n0 += (blockIdx.x % (4 / NT)) * L::kBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, gq = lane >> 5;
@@ -816,8 +818,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_m32(GemmArgs g, int64_
 }
 
 // Whole waves of 256 x 256 tiles (one workgroup per CU); when the last wave
-// would be at most half full, its tiles run as 256 x 128 halves instead, so
-// that wave takes about half as long.
+// would be at most half full, its tiles run as 256 x 128 halves instead, and
+// when at most a quarter full as 256 x 64 quarters, so that wave spreads over
+// the CUs (wgrad's 64 leftover tiles: 128 halves left half the CUs idle).
 template <bool EX>
 static void launch_m32(const GemmArgs& g, int64_t ntiles, int64_t full, int64_t rem, int64_t c, hipStream_t st) {
   const auto groups = [](int64_t n) { return (unsigned)(((n + 7) / 8) * 8); };
@@ -828,7 +831,10 @@ static void launch_m32(const GemmArgs& g, int64_t ntiles, int64_t full, int64_t 
     if (full > 0)
       hipLaunchKernelGGL((k_gemm_m32<4, EX>), dim3(groups(full)), dim3(kGemmThreads), 0, st, g, INT64_C(0),
                          full);
-    hipLaunchKernelGGL((k_gemm_m32<2, EX>), dim3((unsigned)(2 * rem)), dim3(kGemmThreads), 0, st, g, full, rem);
+    if (4 * rem <= c)
+      hipLaunchKernelGGL((k_gemm_m32<1, EX>), dim3((unsigned)(4 * rem)), dim3(kGemmThreads), 0, st, g, full, rem);
+    else
+      hipLaunchKernelGGL((k_gemm_m32<2, EX>), dim3((unsigned)(2 * rem)), dim3(kGemmThreads), 0, st, g, full, rem);
   }
 }
 
