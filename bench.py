@@ -605,7 +605,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
                 "traffic": (rec["bytes_per_launch"] if rec else None),
-                "kernel": "k_gemm_m32<4> (+ k_gemm_m32<2> for a partial last wave of tiles; fp16 MFMA 32x32x16, fp32 accumulate)",
+                "kernel": "k_gemm_m32<4> (+ k_gemm_m32<2> or <1> for a partial last wave of tiles; fp16 MFMA 32x32x16, fp32 accumulate)",
                 "algorithmic_flops_per_launch": gemm_flops,
                 "context_frac_of_fp4_peak": round(achieved / FP4_PEAK_TFLOPS, 4)}
 
