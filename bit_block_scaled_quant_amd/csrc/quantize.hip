@@ -857,10 +857,15 @@ static void launch_cast_transpose_t(const CastTransposeArgs& a, int cus, hipStre
   const bool sr = a.rounding == 1;
   if (a.rht_t) {
     hipLaunchKernelGGL(k_init_amax2, dim3(1), dim3(1), 0, st, a.tensor_scale, a.tensor_scale_t);
-    // four workgroups of four waves per CU, each wave walking several chunks
+    // two workgroups of four waves per CU, each wave walking several chunks
+    // with the next one in flight (X [8192 x 5120]: 5 chunks per wave).  In
+    // a same-process A/B of whole calls, 1 / 2 / 3 / 4 / 5 workgroups per CU
+    // took 60.0 / 56.4 / 59.0 / 61.5 / 63.9 us for X and 263.8 / 247.5 /
+    // 249.3 / 252.2 / 254.9 us for dY: with fewer chunks per wave the loads
+    // of a wave's first chunk are not hidden.
     const int64_t nchunks = (a.rows / 16) * ((a.cols + kAmaxCtCols - 1) / kAmaxCtCols);
     const int blocks = (int)std::max<int64_t>(
-        1, std::min<int64_t>((nchunks + kThreads / 64 - 1) / (kThreads / 64), (int64_t)cus * 4));
+        1, std::min<int64_t>((nchunks + kThreads / 64 - 1) / (kThreads / 64), (int64_t)cus * 2));
     if (amax_cached(a.rows, a.cols, BF16))
       hipLaunchKernelGGL((k_amax_ct<BF16, true>), dim3(blocks), dim3(kThreads), 0, st, a.x, a.rows, a.cols,
                          a.rht_mask, a.tensor_scale, a.tensor_scale_t);
