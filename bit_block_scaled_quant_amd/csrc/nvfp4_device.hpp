@@ -150,9 +150,8 @@ __device__ __forceinline__ uint32_t draw16(const Philox4& p, int j) {  // j in 0
 }
 
 // ------------------------------------------------------------- RHT -------
-// hadamard16: v <- H16 * v by the in-place butterfly h = 1, 2, 4, 8 in fp32,
-// then (QUARTER) the orthonormal 1/4.
-template <bool QUARTER = true>
+// hadamard16: v <- 1/4 * H16 * v: the in-place butterfly h = 1, 2, 4, 8 in
+// fp32, then the factor 1/4 (H16 / 4 is orthonormal).
 __device__ __forceinline__ void hadamard16(float v[16]) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
@@ -164,10 +163,8 @@ __device__ __forceinline__ void hadamard16(float v[16]) {
       v[i + h] = a - b;
     }
   }
-  if (QUARTER) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = 0.25f * v[j];
-  }
+  for (int j = 0; j < 16; ++j) v[j] = 0.25f * v[j];
 }
 
 // max_j |(H16 v)_j| for the amax pass.  The last stage (h = 8) turns the pair
@@ -202,7 +199,7 @@ __device__ __forceinline__ void rht16(float v[16], uint32_t mask) {
 #pragma unroll
   for (int j = 0; j < 16; ++j)
     v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((mask >> j) & 1u) << 31));
-  hadamard16<true>(v);
+  hadamard16(v);
 }
 
 // The same transform on a block held by a lane pair: the even lane holds
@@ -214,7 +211,6 @@ __device__ __forceinline__ float lane_pair_swap(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 
-template <bool QUARTER = true>
 __device__ __forceinline__ void rht16_pair(float v[8], uint32_t mask, bool odd) {
   const uint32_t m8 = odd ? (mask >> 8) : mask;
 #pragma unroll
@@ -236,10 +232,8 @@ __device__ __forceinline__ void rht16_pair(float v[8], uint32_t mask, bool odd) 
     const float p = lane_pair_swap(v[j]);
     v[j] = p + __uint_as_float(__float_as_uint(v[j]) ^ neg);
   }
-  if (QUARTER) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = 0.25f * v[j];
-  }
+  for (int j = 0; j < 8; ++j) v[j] = 0.25f * v[j];
 }
 
 // max_j |(H16 sigma v)_j| over a block held by a lane pair (the transform of

@@ -634,7 +634,7 @@ __global__ __launch_bounds__(kCtThreads, BF16 ? 4 : 2) void k_encode_ct(
       float v[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[j] = chunk_elem<BF16>(ch, j, k);
-      if (RHT) hadamard16<true>(v);
+      if (RHT) hadamard16(v);
       float inv;
       const uint32_t byte = block_scale(max_abs16(v), s_enc_t, inv_tab[1], &inv);
       const int64_t c = c0 + cl + k;
