@@ -17,9 +17,10 @@
 // scales per 32 elements, which cannot represent E4M3 scales per 16.)
 //
 // Two kernels.  k_gemm (any shape): a 256-thread workgroup owns a 256x256
-// tile of C and walks K in steps of 128; packed codes and scale bytes are
-// staged through registers into LDS (double buffered, 16-byte chunks
-// XOR-swizzled against bank conflicts); each wave owns a 128x128 sub-tile,
+// tile of C (128x128 when 256x256 tiles would not fill the CUs) and walks K
+// in steps of 128; packed codes and scale bytes are staged through
+// registers into LDS (double buffered, 16-byte chunks XOR-swizzled against
+// bank conflicts); each wave owns a quarter of the tile,
 // reads its packed fragments from LDS and expands them in registers for
 // v_mfma_f32_16x16x32_f16.  Lane group g = lane / 16 of a fragment covers the
 // 32 K-elements [32g, 32g+32) of a step; its word s feeds MFMA slice s.
