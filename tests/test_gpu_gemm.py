@@ -191,11 +191,12 @@ def test_gemm_full_wgrad():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("M,N", [(8448, 2816), (4096, 4352)])
+@pytest.mark.parametrize("M,N", [(8448, 2816), (4096, 4352), (4096, 4608)])
 def test_gemm_ragged_tile_counts(M, N):
-    # 363 tiles (XCD runs of unequal length, idle workgroups in the last one)
-    # and 272 tiles (a last wave of 256 x 128 halves); sampled outputs against
-    # the oracle, every output written
+    # 363 tiles (XCD runs of unequal length, idle workgroups in the last one),
+    # 272 tiles (a last wave of 256 x 128 halves) and 288 tiles (a last wave
+    # of 256 x 64 quarters after a whole one); sampled outputs against the
+    # oracle, every output written
     K = 512
     a = datagen.host_input(datagen.act(tokens=M, hidden=K, seed=M))
     b = datagen.host_input(datagen.weight(out_features=N, in_features=K, seed=N))
