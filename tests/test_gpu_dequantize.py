@@ -29,7 +29,11 @@ def run(codes, scales, s_enc, dtype):
 
 
 def expect(codes, scales, s_enc, dtype):
-    ref32 = torch.from_numpy(oracle.dequantize(codes, scales, s_enc).astype(np.float32))
+    # a tiny tensor scale takes some values past fp32's range: the cast rounds
+    # them to infinity, as the kernel's single division does (the overflow is
+    # the expected result, not a warning)
+    with np.errstate(over="ignore"):
+        ref32 = torch.from_numpy(oracle.dequantize(codes, scales, s_enc).astype(np.float32))
     return ref32 if dtype == torch.float32 else ref32.to(torch.bfloat16)
 
 
