@@ -16,27 +16,31 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nvfp4_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libnvfp4_oracle.so")
+# a separately built copy of the oracle to load instead (the mutation test
+# runs the pins against deliberately broken copies this way); never rebuilt
+_LIB_OVERRIDE = os.environ.get("NVFP4_ORACLE_LIB")
 _lib = None
 
 F32, BF16 = 0, 1
 RNE, SR = 0, 1
 
 
-def build():
+def build(src=_SRC, out=_LIB_PATH):
     """Compile the oracle with gcc: IEEE binary32 steps, no FMA contraction."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
-           _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+           src, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    os.replace(out + ".tmp", out)
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        path = _LIB_OVERRIDE or _LIB_PATH
+        if not _LIB_OVERRIDE and not os.path.exists(path):
             build()
-        L = ctypes.CDLL(_LIB_PATH)
+        L = ctypes.CDLL(path)
         P, I64, U64, I, F = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
                              ctypes.c_int, ctypes.c_float)
         L.orc_e2m1_value.restype = ctypes.c_double
