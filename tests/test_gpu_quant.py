@@ -114,6 +114,13 @@ def test_edge_cases():
         "ties": torch.tensor([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] * 4).reshape(1, 32)
                 .repeat(16, 1).contiguous(),
         "one_outlier": torch.cat([torch.full((16, 16), 1e-3), torch.full((16, 16), 2688.0)], 1),
+        # S_enc and a block multiplier overflow binary32 and clamp to FLT_MAX
+        "clamped_multiplier": torch.zeros(16, 32).index_put_(
+            (torch.tensor([0, 0, 0, 0, 5]), torch.tensor([0, 16, 17, 18, 20])),
+            torch.tensor([2.0 ** -120, 2.0 ** -128, 2.0 ** -130, -(2.0 ** -129), 2.0 ** -127])),
+        # blocks whose E4M3 scale rounds to zero, holding values up to 3
+        "zero_scale_blocks": torch.cat([torch.full((16, 16), 2.0 ** 40),
+                                        torch.linspace(-3.0, 3.0, 256).reshape(16, 16)], 1),
     }
     for name, x in cases.items():
         x = x.float().contiguous()

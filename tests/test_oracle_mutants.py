@@ -88,8 +88,27 @@ MUTANTS = [
      "    acc_abs += p;\n  }\n  *c = acc;"),
     ("gemm: last product left out", "  for (int64_t k = 0; k < K; ++k) {\n    const double p = deq(",
      "  for (int64_t k = 0; k < K - 1; ++k) {\n    const double p = deq("),
+    ("block amax: signed maximum", "        if (fabsf(blk[j]) > amax_b) amax_b = fabsf(blk[j]);",
+     "        if (blk[j] > amax_b) amax_b = blk[j];"),
+    ("tensor scale: overflow not clamped", "  if (isinf(s)) s = FLT_MAX;\n  return s;", "  return s;"),
+    ("multiplier: overflow not clamped", "*inv = isinf(q) ? FLT_MAX : q;", "*inv = q;"),
+    ("multiplier: zero-scale block passes x through", "    *inv = 0.0f;\n  } else {", "    *inv = 1.0f;\n  } else {"),
+    ("tensor scale: amax written as S_enc", "  tensor_scale[0] = s_enc;\n  tensor_scale[1] = amax;\n\n  /* rowwise",
+     "  tensor_scale[0] = s_enc;\n  tensor_scale[1] = s_enc;\n\n  /* rowwise"),
+    ("2D: transposed draw index", "seed, 0u, (uint64_t)(r * cols + c));\n          put_code(codes + r",
+     "seed, 0u, (uint64_t)(c * rows + r));\n          put_code(codes + r"),
+    ("2D: transposed scale of the wrong tile", "scales_t[(tc * 16 + j) * (rows / 16) + tr] = byte;",
+     "scales_t[(tc * 16 + j) * (rows / 16) + tc % (rows / 16)] = byte;"),
+    ("dequantize: nibbles swapped",
+     "(k & 1) ? (byte >> 4) : (byte & 0x0F);\n  return orc_e2m1_value(code) * orc_e4m3_value",
+     "(k & 1) ? (byte & 0x0F) : (byte >> 4);\n  return orc_e2m1_value(code) * orc_e4m3_value"),
+    ("rht: difference the wrong way round", "v[i + h] = a - b;", "v[i + h] = b - a;"),
+    ("draws: array form off by one", "orc_sr_bits(seed, stream, first + (uint64_t)i);",
+     "orc_sr_bits(seed, stream, first + (uint64_t)i + 1);"),
     # MXFP4
     ("mx: scale exponent one too small", "int s = (e - 1) - 2;", "int s = (e - 1) - 1;"),
+    ("mx: zero block takes byte 1", "if (amax == 0.0f) return -127;", "if (amax == 0.0f) return -126;"),
+    ("mx: exponent not clamped below", "  if (s < -127) s = -127;\n", ""),
     ("mx: 16-element scale blocks in the GEMM", "orc_e8m0_value(scales[i * (K / 32) + k / 32])",
      "orc_e8m0_value(scales[i * (K / 32) + k / 16])"),
 ]

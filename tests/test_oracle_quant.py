@@ -417,3 +417,61 @@ def test_block_scale_rounds_the_product_then_the_quotient(orc):
             sensitive += alt != want
     print(f"blocks whose byte the other rounding order would change: {sensitive}")
     assert sensitive >= 20, sensitive
+
+
+def test_overflowing_multipliers_clamp_to_flt_max(orc):
+    """A tensor so small that S_enc and a block multiplier overflow binary32
+    (readings R1, R3: both clamp to FLT_MAX).  Closed forms, with
+    FLT_MAX = (2 - 2^-23) 2^127:
+    * amax 2^-120: 2688 * 2^120 overflows, so S_enc = FLT_MAX;
+    * block 0 (amax 2^-120): t = FLT_MAX 2^-120 = 256 - 2^-16, s = t / 6 = 42.67,
+      nearest E4M3 44 (byte 0x63); its amax element gives y = 5.82 -> 6 (code 7);
+    * block 1 (amax 2^-128): t = 1 - 2^-24, s = 0.1667 -> E4M3 0.171875 (byte
+      0x23); S_enc / 0.171875 overflows, so the multiplier is FLT_MAX and
+      y = x FLT_MAX: 2^-128 -> 1 - 2^-24 (code 2), 2^-130 -> 0.25 - 2^-26
+      (code 0), -2^-129 -> -(0.5 - 2^-25) (code 0x9).  An unclamped (infinite)
+      multiplier would saturate all three to 6."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = 2.0 ** -120
+    x[0, 16], x[0, 17], x[0, 18] = 2.0 ** -128, 2.0 ** -130, -(2.0 ** -129)
+    codes, scales, ts, _, _ = orc.quantize_1d(x)
+    assert ts[0] == np.finfo(np.float32).max and ts[1] == np.float32(2.0 ** -120)
+    assert list(scales[0]) == [0x63, 0x23]
+    q = unpack(codes)[0]
+    assert q[0] == 7 and not q[1:16].any()
+    assert list(q[16:19]) == [2, 0, 9] and not q[19:].any()
+
+
+def test_zero_scale_block_gives_signed_zero_codes(orc):
+    """A block whose scale rounds to E4M3 zero (amax_b S_enc / 6 below 2^-10)
+    takes the multiplier 0 (reading R3): every element encodes to a zero code
+    that keeps its sign, however large the element itself is.  Here the
+    tensor amax is 2^40 and block 1 holds values up to 3, i.e. s = 3 * 2688 *
+    2^-40 / 6 < 2^-29."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = 2.0 ** 40
+    x[0, 16:24] = [1.0, -3.0, 2.5, -0.5, 0.0, -0.0, 3.0, 1.75]
+    codes, scales, ts, _, _ = orc.quantize_1d(x)
+    assert scales[0, 1] == 0
+    q = unpack(codes)[0, 16:24]
+    assert list(q) == [0, 8, 0, 8, 0, 8, 0, 0]
+
+
+def test_sr_2d_brute_force(orc):
+    """2D blocks with SR (section 2B.3, reading R6): each element takes the
+    draw of its own index r * cols + c of W in stream 0 and the codec's rule
+    under the multiplier of its 16 x 16 tile; both copies carry the same code."""
+    rows, cols = 32, 48
+    w = datagen.weight(out_features=rows, in_features=cols, seed=12)
+    xf = w.float().numpy()
+    seed = 31
+    codes, scales, ts, ct, st = orc.quantize_2d(datagen.bf16_bits(w), rounding=1, seed=seed)
+    s_enc = ts[0]
+    q = unpack(codes)
+    for r in range(rows):
+        for c in range(cols):
+            sb = np.float32(orc.e4m3_value(scales[r, c // 16]))
+            inv = np.float32(s_enc) / sb if sb != 0 else np.float32(0)
+            y = np.float32(xf[r, c]) * inv
+            assert q[r, c] == orc.e2m1_encode_sr(y, orc.sr_bits(seed, 0, r * cols + c)), (r, c)
+    assert np.array_equal(unpack(ct), q.T)
