@@ -465,20 +465,30 @@ __device__ __forceinline__ void sr_cvt(uint32_t& w, float v, uint32_t rand) {
     asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,1]" : "+v"(w) : "v"(src), "v"(rand), "s"(sc));
 }
 
-// elements 2K (draw: low half of word K) and 2K + 1 (high half) into byte K
-// of the even / odd code words; rand = ~(u << 16) from the complemented word
+// ~(w << 16), i.e. the complemented low half of w in the high half and ones
+// below, in one instruction: v_mad_i32_i24 forms sext24(w) * -2^16 - 1, whose
+// low 32 bits depend on the low 16 bits of w only.  (Written out, the
+// compiler emits a shift and a complement.)
+__device__ __forceinline__ uint32_t not_low_half_up(uint32_t w) {
+  uint32_t r;
+  asm("v_mad_i32_i24 %0, %1, %2, -1" : "=v"(r) : "v"(w), "s"(-65536));
+  return r;
+}
+
+// elements 2K (draw: low half of word w) and 2K + 1 (high half) into byte K
+// of the even / odd code words; rand = ~(u << 16) for draw u
 template <int K>
-__device__ __forceinline__ void sr_pair(const float* y, uint32_t nw, uint32_t& we, uint32_t& wo) {
-  sr_cvt<K>(we, y[2 * K], (nw << 16) | 0xFFFFu);
-  sr_cvt<K>(wo, y[2 * K + 1], nw | 0xFFFFu);
+__device__ __forceinline__ void sr_pair(const float* y, uint32_t w, uint32_t& we, uint32_t& wo) {
+  sr_cvt<K>(we, y[2 * K], not_low_half_up(w));
+  sr_cvt<K>(wo, y[2 * K + 1], ~w | 0xFFFFu);
 }
 
 __device__ __forceinline__ uint32_t e2m1_sr8(const float* y, const Philox4& p) {
   uint32_t we = 0, wo = 0;  // codes of even / odd elements, one per byte
-  sr_pair<0>(y, ~p.x, we, wo);
-  sr_pair<1>(y, ~p.y, we, wo);
-  sr_pair<2>(y, ~p.z, we, wo);
-  sr_pair<3>(y, ~p.w, we, wo);
+  sr_pair<0>(y, p.x, we, wo);
+  sr_pair<1>(y, p.y, we, wo);
+  sr_pair<2>(y, p.z, we, wo);
+  sr_pair<3>(y, p.w, we, wo);
   return we | (wo << 4);
 }
 
