@@ -277,3 +277,31 @@ def test_gemm_same_sign_large_k(M, N):
     torch.cuda.synchronize()
     worst = check_every_output(c, ra, rb)
     print(f"same sign {M}x{N}x{K}: worst |err| / sum|ab| = {worst:.3g}", flush=True)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("K", [1 << 24, (1 << 24) + 512])
+def test_gemm_largest_k_either_side_of_the_fast_path_limit(K):
+    """The whole-tile kernel forms operand offsets in 32 bits and takes K up
+    to 2^24; one step more goes to the general kernel, whose offsets are 64
+    bit.  A 256 x 256 product at K = 2^24 and 2^24 + 512 (random codes and
+    scale bytes, 2 GiB per operand) against the oracle's double sums at the
+    four corners and 60 random outputs."""
+    M = N = 256
+    g = torch.Generator(device=DEV).manual_seed(K)
+    ac = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=DEV, generator=g)
+    bc = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=DEV, generator=g)
+    asc = torch.randint(0x28, 0x48, (M, K // 16), dtype=torch.uint8, device=DEV, generator=g)
+    bsc = torch.randint(0x28, 0x48, (N, K // 16), dtype=torch.uint8, device=DEV, generator=g)
+    ta = torch.tensor([3.0, 1.0], device=DEV)
+    tb = torch.tensor([0.75, 1.0], device=DEV)
+    c = nv.gemm(nv.Quantized(ac, asc, ta), nv.Quantized(bc, bsc, tb))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(K)
+    ii = np.concatenate([[0, 0, M - 1, M - 1], rng.integers(0, M, 60)]).astype(np.int64)
+    jj = np.concatenate([[0, N - 1, 0, N - 1], rng.integers(0, N, 60)]).astype(np.int64)
+    ref, refabs = oracle.gemm_sample(ac.cpu().numpy(), asc.cpu().numpy(), 3.0, bc.cpu().numpy(),
+                                     bsc.cpu().numpy(), 0.75, ii, jj)
+    got = c[torch.from_numpy(ii).to(DEV), torch.from_numpy(jj).to(DEV)].cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    assert np.all(err <= TOL * refabs), np.max(err / refabs)
