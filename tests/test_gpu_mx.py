@@ -127,3 +127,28 @@ def test_mx_gemm_full_size_sampled(name, M, N, K, ka, kb):
     ii = np.concatenate([rng.integers(0, M, 2048), [0, M - 1, 255, 256]])
     jj = np.concatenate([rng.integers(0, N, 2048), [N - 1, 0, 256, 255]])
     check_gemm(ac, as_, bc, bs, sample=(ii, jj))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("K", [1 << 24, (1 << 24) + 256])
+def test_mx_gemm_largest_k_either_side_of_the_fast_path_limit(K):
+    """The fast MXFP4 kernel takes K up to 2^24 (32-bit operand offsets);
+    2^24 + 256 goes to the general kernel.  A 256 x 256 product of random
+    codes and E8M0 bytes (2 GiB per operand) against the oracle at the four
+    corners and 60 random outputs."""
+    M = N = 256
+    g = torch.Generator(device=DEV).manual_seed(K)
+    ac = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=DEV, generator=g)
+    bc = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=DEV, generator=g)
+    as_ = torch.randint(118, 136, (M, K // 32), dtype=torch.uint8, device=DEV, generator=g)
+    bs = torch.randint(118, 136, (N, K // 32), dtype=torch.uint8, device=DEV, generator=g)
+    c = nv.mx_gemm(nv.MxQuantized(ac, as_), nv.MxQuantized(bc, bs))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(K)
+    ii = np.concatenate([[0, 0, M - 1, M - 1], rng.integers(0, M, 60)]).astype(np.int64)
+    jj = np.concatenate([[0, N - 1, 0, N - 1], rng.integers(0, N, 60)]).astype(np.int64)
+    ref, absum = oracle.mx_gemm(ac.cpu().numpy(), as_.cpu().numpy(), bc.cpu().numpy(), bs.cpu().numpy(),
+                                ii, jj)
+    got = c[torch.from_numpy(ii).to(DEV), torch.from_numpy(jj).to(DEV)].cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-5 * absum), np.max(err / absum)
