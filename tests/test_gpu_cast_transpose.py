@@ -109,3 +109,20 @@ def test_cast_transpose_full_size(name, gen, rounding):
     row, col = oracle_pair(datagen.host_input(x), rounding, 0, 0, 1, 0)
     assert_same(q, row, "rowwise")
     assert_same(qt, col, "columnwise")
+
+
+@pytest.mark.timeout(900)
+def test_cast_transpose_more_than_2_31_elements():
+    """A 16400 x 131072 gradient-like bf16 tensor (2^31 + 2^24 elements) through
+    the cast-transpose with SR and the transform on the columnwise copy, both
+    copies bit for bit against the oracle: offsets and SR draw indices pass
+    2^31 in both layouts."""
+    x = datagen.grad(DEV, seed=4, tokens=16400, out_features=131072)
+    assert x.numel() > 2 ** 31
+    q, qt = nv.quantize_cast_transpose(x, rounding=1, seed=5, seed_t=6, rht_t=True, rht_seed=77)
+    torch.cuda.synchronize()
+    xh = datagen.host_input(x)
+    del x
+    row, col = oracle_pair(xh, 1, 5, 6, 1, 77)
+    assert_same(q, row, "rowwise")
+    assert_same(qt, col, "columnwise")

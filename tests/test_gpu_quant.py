@@ -199,3 +199,16 @@ def test_full_size_sweep(rows, cols, two_d, rounding):
         torch.cuda.synchronize()
         ref = oracle.quantize_1d(datagen.host_input(x), rounding=rounding, seed=0, transposed=True)
     assert_same(q, ref, True)
+
+
+@pytest.mark.timeout(900)
+def test_more_than_2_31_elements():
+    """A 16400 x 131072 bf16 tensor (2^31 + 2^24 elements, 4.3 GB) quantized
+    1D with SR and its columnwise copy, bit for bit against the oracle: every
+    element offset, code byte offset and SR draw index passes 2^31."""
+    x = datagen.act(DEV, seed=5, tokens=16400, hidden=131072)
+    assert x.numel() > 2 ** 31
+    q = nv.quantize(x, rounding=1, seed=3, transposed=True)
+    torch.cuda.synchronize()
+    ref = oracle.quantize_1d(datagen.host_input(x), rounding=1, seed=3, transposed=True)
+    assert_same(q, ref, True)
