@@ -43,7 +43,12 @@
  *     surface at the caller's next synchronization.
  *   - Inputs must be finite: NaN or Inf inputs are outside the contract and
  *     are not detected.
- *   - Thread-safe: no state besides a per-device cache of the CU count.
+ *   - Sizes: a tensor holds at most 2^40 elements (rows * cols); a GEMM's
+ *     M * K, N * K and M * N are each at most 2^40, with M at most
+ *     65535 * 128 (NVFP4) or 65535 * 64 (MXFP4).  Larger sizes give
+ *     NVFP4_ERR_SHAPE.
+ *   - Thread-safe: no state besides a per-device cache of the CU count and
+ *     each thread's last error text.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
