@@ -121,6 +121,8 @@ def test_mx_calls_reject_bad_arguments():
     assert g(A16, A16, A16, A16, 0, 16, 64, A16, None) == -2
     assert g(None, A16, A16, A16, 16, 16, 64, A16, None) == -1
     assert g(A8, A16, A16, A16, 16, 16, 64, A16, None) == -3    # codes 16-byte aligned
+    assert g(A16, A16, A16, A16, 65535 * 64 + 64, 16, 64, A16, None) == -2   # M above the grid limit
+    assert g(A16, A16, A16, A16, 1 << 21, 16, 1 << 20, A16, None) == -2      # M * K above 2^40
 
 
 def test_gemm_ex_and_quantize_with_amax_reject_bad_arguments():
@@ -149,6 +151,10 @@ def test_rht_and_gemm_reject_bad_arguments():
     assert g(A16, A16, A16, A16, A16, A16, 0, 16, 32, A16, None) == -2
     assert g(None, A16, A16, A16, A16, A16, 16, 16, 32, A16, None) == -1
     assert g(ctypes.c_void_p(0x10004), A16, A16, A16, A16, A16, 16, 16, 32, A16, None) == -3
+    assert g(A16, A16, A16, A16, A16, A16, 65535 * 128 + 16, 16, 32, A16, None) == -2  # M above the grid limit
+    assert g(A16, A16, A16, A16, A16, A16, 1 << 21, 16, 1 << 20, A16, None) == -2      # M * K above 2^40
+    assert g(A16, A16, A16, A16, A16, A16, 16, 1 << 21, 1 << 20, A16, None) == -2      # N * K above 2^40
+    assert g(A16, A16, A16, A16, A16, A16, 1 << 20, 1 << 21, 16, A16, None) == -2      # M * N above 2^40
 
 
 def test_no_cpu_fallback():
