@@ -305,3 +305,20 @@ def test_gemm_largest_k_either_side_of_the_fast_path_limit(K):
     got = c[torch.from_numpy(ii).to(DEV), torch.from_numpy(jj).to(DEV)].cpu().numpy().astype(np.float64)
     err = np.abs(got - ref)
     assert np.all(err <= TOL * refabs), np.max(err / refabs)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M,N,K", [(4000, 5008, 1040), (4452, 3600, 528)])
+def test_gemm_general_path_large_ragged(M, N, K):
+    """Shapes off the whole-tile kernel's grid with enough 256 x 256 tiles
+    to fill the chip (16 x 20 and 18 x 15, ragged at the bottom and right),
+    so the general kernel runs its large tiles, with K not a multiple of its
+    128-element step: every output against the oracle's dense form."""
+    a = datagen.host_input(datagen.act(tokens=M, hidden=K, seed=K))
+    b = datagen.host_input(datagen.weight(out_features=N, in_features=K, seed=N))
+    ra, rb = oracle.quantize_1d(a), oracle.quantize_1d(b, rounding=1, seed=4)
+    c = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    nv.gemm(upload(ra), upload(rb), out=c)
+    torch.cuda.synchronize()
+    assert torch.isfinite(c).all()
+    check_every_output(c, ra, rb)
