@@ -108,6 +108,28 @@ MUTANTS = [
     # MXFP4
     ("mx: scale exponent one too small", "int s = (e - 1) - 2;", "int s = (e - 1) - 1;"),
     ("mx: zero block takes byte 1", "if (amax == 0.0f) return -127;", "if (amax == 0.0f) return -126;"),
+    ("mx: elements scaled one binade off", "ldexp((double)load_elem(x, dtype, r * cols + 32 * b + k), -s)",
+     "ldexp((double)load_elem(x, dtype, r * cols + 32 * b + k), -s + 1)"),
+    ("mx: block amax over half the block", "      for (int k = 0; k < 32; ++k) {\n        const float a = fabsf(",
+     "      for (int k = 0; k < 16; ++k) {\n        const float a = fabsf("),
+    ("mx: E8M0 bias 128", "return ldexp(1.0, (byte & 0xFF) - 127);", "return ldexp(1.0, (byte & 0xFF) - 128);"),
+    ("mx: dequantize nibbles swapped", "(k & 1) ? (byte >> 4) : (byte & 0x0F);\n  return orc_e2m1_value(code) * orc_e8m0_value",
+     "(k & 1) ? (byte & 0x0F) : (byte >> 4);\n  return orc_e2m1_value(code) * orc_e8m0_value"),
+    ("rht: sign word from output word 1", "  return out[0] & 0xFFFFu;", "  return out[1] & 0xFFFFu;"),
+    ("rht: one sign of the mask flipped", "      rht16(v, mask);", "      rht16(v, mask ^ 1u);"),
+    ("philox: key halves swapped in the draws",
+     "const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};",
+     "const uint32_t key[2] = {(uint32_t)(seed >> 32), (uint32_t)seed};"),
+    ("e4m3 decode: NaN at 0x7E", "if (e == 15 && m == 7) return NAN;", "if (e == 15 && m == 6) return NAN;"),
+    ("dequantize: sign dropped", "return orc_e2m1_value(code) * orc_e4m3_value(scales[i * (K / 16) + k / 16]) / s_enc;",
+     "return orc_e2m1_value(code & 7) * orc_e4m3_value(scales[i * (K / 16) + k / 16]) / s_enc;"),
+    ("gemm: accumulated in float", "    const double p = deq(a_codes, a_scales, sa, K, i, k) * deq(b_codes, b_scales, sb, K, j, k);\n    acc += p;",
+     "    const double p = deq(a_codes, a_scales, sa, K, i, k) * deq(b_codes, b_scales, sb, K, j, k);\n    acc = (float)(acc + p);"),
+    ("input check: infinities accepted", "if (!isfinite(load_elem(x, dtype, i))) bad = 1;",
+     "if (isnan(load_elem(x, dtype, i))) bad = 1;"),
+    ("block scale: zero test on the wrong side", "  if (sb == 0.0f) {", "  if (sb < 0.0f) {"),
+    ("quantize: transform ignored", "  if (rht) {\n    orc_rht(x, dtype, rows, cols, rht_seed, v);",
+     "  if (0) {\n    orc_rht(x, dtype, rows, cols, rht_seed, v);"),
     ("mx: exponent not clamped below", "  if (s < -127) s = -127;\n", ""),
     ("mx: 16-element scale blocks in the GEMM", "orc_e8m0_value(scales[i * (K / 32) + k / 32])",
      "orc_e8m0_value(scales[i * (K / 32) + k / 16])"),
